@@ -1,0 +1,257 @@
+/*
+ * sortformer.h — C ABI of the MI355X (gfx950) Streaming Sortformer /
+ * Nemotron-3-style speaker-diarization forward.
+ *
+ * The library computes, on one GPU, the frame-classification forward the
+ * pages describe: 128-bin log-mel frontend, 8x ConvSubsampling (pre_encode),
+ * 17 FastConformer layers, encoder_proj, 18 Transformer layers and a sigmoid
+ * speaker head ("Streaming Sortformer Diarizer" model card, Pipeline), run
+ * over the [speaker_cache | FIFO | chunk] window with FIFO pops and log-odds
+ * speaker-cache compression (same card, Streaming Architecture). The
+ * Nemotron-3-style variant (8x stacked mel, 31 RoPE transformer layers,
+ * 8 speakers, ConvTranspose 10 ms head) follows the model-card summary in
+ * the ExecuTorch issue "Enable Nemotron-3-Diarization on MLX, CUDA, XNNPACK,
+ * and Vulkan".
+ *
+ * Conventions for every call:
+ *  - Pointers prefixed d_ are device (HIP) pointers; all others are host.
+ *  - The caller allocates every device buffer (weights, workspace, state)
+ *    with the sizes the *_bytes queries return; the library never keeps a
+ *    reference to caller host memory after a call returns.
+ *  - `stream` is a hipStream_t passed as void* (NULL = default stream).
+ *    Compute calls only enqueue work on that stream and return without
+ *    waiting for it, unless documented otherwise.
+ *  - Every call returns an sf_status; on error nothing is enqueued and
+ *    caller outputs are left untouched. HIP errors are mapped to SF_EHIP,
+ *    never thrown. Calls on one model/stream object are not thread-safe.
+ *  - Tensors are row-major, batch-major: (B, rows, cols), fp32 unless stated.
+ */
+#ifndef SORTFORMER_H
+#define SORTFORMER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t sf_status;
+#define SF_OK 0
+#define SF_EINVAL (-1)        /* bad argument (null pointer, unknown enum)      */
+#define SF_ESHAPE (-2)        /* size outside the supported range               */
+#define SF_ENOMEM (-3)        /* caller buffer smaller than the size query      */
+#define SF_EHIP (-4)          /* a HIP runtime call failed                      */
+#define SF_ESTATE (-5)        /* call not allowed in the stream's current state */
+#define SF_EUNSUPPORTED (-6)  /* combination not implemented                    */
+
+#define SF_ARCH_SORTFORMER 0  /* 4 speakers, conformer + transformer, 80 ms out */
+#define SF_ARCH_NEMOTRON 1    /* 8 speakers, RoPE transformer, 10 ms out        */
+#define SF_DTYPE_F32 0        /* every GEMM operand fp32                         */
+#define SF_DTYPE_BF16 1       /* GEMM/attention operands bf16, fp32 accumulate   */
+#define SF_INIT_SPEC 0        /* weights N(0,0.02^2), biases 0, norms gamma 1    */
+#define SF_INIT_FULL_RANDOM 1 /* also biases/norm params/BN stats random        */
+
+/* Longest encoder window (frames of 80 ms) any call accepts; the relative
+ * position and rotary tables are sized for it. The pages' own exported
+ * encoder accepts at most 1000 frames (model card, Exported Methods). */
+#define SF_MAX_WINDOW 1024
+
+typedef struct sf_model_config {
+  int32_t arch;      /* SF_ARCH_*                                 */
+  int32_t dtype;     /* SF_DTYPE_*                                */
+  int32_t init_mode; /* SF_INIT_*                                 */
+  int32_t n_spk;     /* 4 for SORTFORMER, 8 for NEMOTRON (checked) */
+} sf_model_config;
+
+/* Streaming window configuration, all in 80 ms encoder frames (model card,
+ * Streaming Configurations; latency = (chunk_len + right_context) x 80 ms). */
+typedef struct sf_stream_config {
+  int32_t chunk_len;     /* frames scored per step                           */
+  int32_t right_context; /* look-ahead frames attended but not scored        */
+  int32_t fifo_len;      /* FIFO capacity before frames pop into the cache   */
+  int32_t update_period; /* minimum frames popped per overflow               */
+  int32_t spkcache_len;  /* speaker-cache size after compression (188)       */
+  int32_t n_sil_per_spk; /* silence placeholders guaranteed per speaker (3)  */
+} sf_stream_config;
+
+typedef struct sf_model sf_model;   /* opaque, host-side */
+typedef struct sf_stream sf_stream; /* opaque, host-side */
+
+/* Human-readable text for a status code (static storage). */
+const char* sortformer_status_string(sf_status status);
+
+/* Named presets: "very_high" 340/40/40/300/188, "high" 124/1/124/124/188,
+ * "low" 6/7/188/144/188, "ultra_low" 3/1/188/144/188 (model card, Streaming
+ * Configurations) and "nemotron_offline" 380/0/188/192/188 (30.4 s chunks,
+ * Transformers docs "Nemotron 3 Diarization", Overview). SF_EINVAL if the
+ * name is unknown. */
+sf_status sortformer_stream_preset(const char* name, sf_stream_config* out);
+
+/* ------------------------------------------------------------------ model */
+
+/* Device bytes the weights (plus derived tables) need; 0 if cfg is invalid. */
+size_t sortformer_weight_bytes(const sf_model_config* cfg);
+
+/* Generate the seeded random-init weights on the host (SplitMix64 counters +
+ * Box-Muller, one stream per tensor), upload them into d_weights (caller
+ * memory of >= sortformer_weight_bytes bytes, 256-byte aligned), derive the
+ * device tables (relative-position projections, folded BatchNorm, DFT/mel
+ * tables) and return a host handle. Blocks until the uploads are done.
+ * d_weights must stay allocated until sortformer_free. */
+sf_status sortformer_init(const sf_model_config* cfg, uint64_t seed, void* d_weights,
+                          size_t weight_bytes, void* stream, sf_model** out);
+void sortformer_free(sf_model* model);
+sf_status sortformer_get_config(const sf_model* model, sf_model_config* out);
+
+/* Canonical tensor list (name, element count) and the fp32 value of every
+ * element as generated (before any bf16 rounding); for checking the weight
+ * generator. name_cap bytes are written at most (NUL-terminated). */
+int32_t sortformer_num_tensors(const sf_model* model);
+sf_status sortformer_tensor_info(const sf_model* model, int32_t index, char* name,
+                                 int32_t name_cap, int64_t* numel);
+sf_status sortformer_get_weights(const sf_model* model, int32_t index, float* host_out);
+
+/* Host-only variants (no device needed): tensor count of a configuration,
+ * and tensor `index` generated for `seed` — name (at most name_cap bytes),
+ * element count and, if host_out is not NULL, its fp32 values. */
+int32_t sortformer_config_num_tensors(const sf_model_config* cfg);
+sf_status sortformer_config_tensor(const sf_model_config* cfg, uint64_t seed, int32_t index,
+                                   char* name, int32_t name_cap, int64_t* numel,
+                                   float* host_out);
+
+/* ---------------------------------------------------------------- offline */
+
+/* Workspace bytes for sortformer_forward_offline on `batch` clips of
+ * n_samples samples each (0 if unsupported). */
+size_t sortformer_offline_workspace_bytes(const sf_model* model, int32_t batch,
+                                          int64_t n_samples);
+
+/* Offline forward (NeMo SortformerEncLabelModel.forward: audio -> per-frame
+ * sigmoid speaker activity).
+ *  d_audio: (B, N) fp32 16 kHz mono. d_probs: (B, n_out, S) fp32 output.
+ *  SORTFORMER: n_out = ceil(floor(N/160)/8) frames of 80 ms; needs
+ *    n_out <= SF_MAX_WINDOW (the whole clip is one encoder window).
+ *  NEMOTRON: the clip is processed in 30.4 s chunks with the arrival-order
+ *    speaker cache and FIFO ("nemotron_offline" preset) and n_out =
+ *    8*ceil(floor(N/160)/8) frames of 10 ms; any N.
+ * *n_out_host receives n_out before any work is enqueued. */
+sf_status sortformer_forward_offline(sf_model* model, const float* d_audio, int32_t batch,
+                                     int64_t n_samples, float* d_probs, int64_t* n_out_host,
+                                     void* d_workspace, size_t workspace_bytes, void* stream);
+
+/* -------------------------------------------------------------- streaming */
+
+/* Device bytes of the per-stream state (speaker cache, FIFO, look-ahead
+ * embeddings and their probabilities, placeholder flags, silence sums, audio
+ * ring) for `batch` lockstep streams; and of the step workspace. */
+size_t sortformer_state_bytes(const sf_model* model, const sf_stream_config* scfg,
+                              int32_t batch);
+size_t sortformer_stream_workspace_bytes(const sf_model* model, const sf_stream_config* scfg,
+                                         int32_t batch);
+
+/* Bind a state object to caller memory d_state and reset it. The B streams
+ * advance in lockstep (identical lengths, per-stream contents). */
+sf_status sortformer_stream_create(sf_model* model, const sf_stream_config* scfg, int32_t batch,
+                                   void* d_state, size_t state_bytes, void* stream,
+                                   sf_stream** out);
+void sortformer_stream_destroy(sf_stream* st);
+/* Empty the cache/FIFO/audio history (a new recording); enqueued on stream. */
+sf_status sortformer_stream_reset(sf_stream* st, void* stream);
+
+/* Samples per stream the next non-final step needs (like the Transformers
+ * processor's num_samples_first_audio_chunk / num_samples_per_audio_chunk):
+ * step 0 needs 1280*(chunk+right_context)+40, later steps 1280*chunk. */
+int64_t sortformer_stream_samples_needed(const sf_stream* st);
+/* Upper bound of frames any step emits per stream (for sizing d_probs_out):
+ * chunk_len for SORTFORMER, 8*chunk_len for NEMOTRON. */
+int32_t sortformer_stream_max_emit(const sf_stream* st);
+
+/* One streaming step (NeMo forward_streaming_step; Transformers model call
+ * with speaker_cache): append n_new samples per stream (d_audio_new (B,
+ * n_new)), compute the new mel frames and pre-encode only the new encoder
+ * frames, run the encoder over [cache | FIFO | chunk | look-ahead], write the
+ * chunk's probabilities to d_probs_out (B, n_emitted, S), refresh the FIFO
+ * predictions, append the chunk to the FIFO, pop into the cache and compress
+ * the cache when it overflows.
+ * Non-final steps need n_new == sortformer_stream_samples_needed. With
+ * is_last != 0 the clip ends after these n_new samples (any count >= 0): the
+ * step has no look-ahead and emits every remaining frame; later steps return
+ * SF_ESTATE until sortformer_stream_reset. *n_emitted_host is set before any
+ * work is enqueued. No allocation and no host synchronisation. */
+sf_status sortformer_stream_step(sf_stream* st, const float* d_audio_new, int64_t n_new,
+                                 int32_t is_last, float* d_probs_out, int32_t* n_emitted_host,
+                                 void* d_workspace, size_t workspace_bytes, void* stream);
+
+/* State introspection for checkpoint/resume and tests.
+ * info (host, 8 values): cache_len, fifo_len, lookahead_len, capacity rows,
+ *   steps_done, frames_emitted, samples_received, finished.
+ * ptrs (host, 6 values): device pointers of emb (B,cap,D) fp32, probs
+ *   (B,cap,S) fp32, placeholder flags (B,cap) int32, silence sum (B,D) fp64,
+ *   silence count (B) int32, and the model dimension D as an integer.
+ * Rows [0,cache_len) are the cache, then the FIFO, then look-ahead rows. */
+sf_status sortformer_stream_get_info(const sf_stream* st, int64_t* info, void** ptrs);
+/* Checkpoint/resume of the cache content: copy the rows [0, cache_len +
+ * fifo_len + lookahead_len) of the state to host memory (export) or from
+ * host memory (import, which also sets the three lengths). Host layouts:
+ * emb (B, rows, D) fp32, probs (B, rows, S) fp32, flags (B, rows) int32
+ * (1 = silence placeholder), sil_sum (B, D) fp64, sil_cnt (B) int32.
+ * Both block until the copies are done. Import checks the lengths against
+ * the configuration (cache <= spkcache_len, fifo <= fifo_len, look-ahead <=
+ * chunk_len + right_context). */
+sf_status sortformer_stream_export(const sf_stream* st, float* emb, float* probs, int32_t* flags,
+                                   double* sil_sum, int32_t* sil_cnt, void* stream);
+sf_status sortformer_stream_import(sf_stream* st, int32_t cache_len, int32_t fifo_len,
+                                   int32_t lookahead_len, const float* emb, const float* probs,
+                                   const int32_t* flags, const double* sil_sum,
+                                   const int32_t* sil_cnt, void* stream);
+
+/* Test hook — the cache update alone (FIFO prediction refresh, chunk append,
+ * pop with silence statistics, compression), given window probabilities
+ * d_window_probs (B, W, S) with W = cache_len + fifo_len + lookahead_len of
+ * the current state; the first n_chunk look-ahead rows are the chunk. */
+sf_status sortformer_stream_update(sf_stream* st, const float* d_window_probs, int32_t n_chunk,
+                                   void* d_workspace, size_t workspace_bytes, void* stream);
+
+/* Test hook — the encoder alone on explicit window embeddings: d_emb (B, W,
+ * 512) fp32 pre-encoded frames, rows >= n_valid are right padding (masked
+ * keys, zeroed conv input). Writes d_probs (B, W, S) at 80 ms and, for
+ * NEMOTRON, d_probs10 (B, 8W, S) (may be NULL for SORTFORMER). */
+size_t sortformer_encode_workspace_bytes(const sf_model* model, int32_t batch, int32_t window);
+sf_status sortformer_encode_window(sf_model* model, const float* d_emb, int32_t batch,
+                                   int32_t window, int32_t n_valid, float* d_probs,
+                                   float* d_probs10, void* d_workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/* Test hook — frontend and pre_encode alone: d_audio (B, N) -> d_mel (B, T,
+ * 128) with T = floor(N/160), and -> d_emb (B, ceil(T/8), 512). Either
+ * output may be NULL. Workspace: sortformer_pre_encode_workspace_bytes. */
+size_t sortformer_pre_encode_workspace_bytes(const sf_model* model, int32_t batch,
+                                             int64_t n_samples);
+sf_status sortformer_pre_encode(sf_model* model, const float* d_audio, int32_t batch,
+                                int64_t n_samples, float* d_mel, float* d_emb,
+                                void* d_workspace, size_t workspace_bytes, void* stream);
+
+/* --------------------------------------------------------------- profiling */
+
+/* Benchmark aid: while a kernel class is profiled, every launch of that
+ * class is bracketed by a pair of HIP events recorded on the launch's stream,
+ * and the launch's algorithmic flop and byte counts are added up (what the
+ * operation must compute and move). One class at a time; at most
+ * max_launches launches are timed. Not thread-safe. */
+#define SF_PROF_GEMM 1
+#define SF_PROF_ATTN 2
+#define SF_PROF_LN 3
+#define SF_PROF_CONV 4
+#define SF_PROF_FRONTEND 5
+#define SF_PROF_CACHE 6
+sf_status sortformer_profile_begin(int32_t kernel_class, int32_t max_launches);
+/* Waits for the recorded events; returns the summed kernel time (ms), the
+ * launch count and the algorithmic flops and bytes of those launches. */
+sf_status sortformer_profile_end(double* total_ms, int64_t* launches, double* flops,
+                                 double* bytes);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SORTFORMER_H */

@@ -34,11 +34,15 @@ def nemotron_encoder(w):
     return lambda window: nemotron.encode_window(w, window)
 
 
-def sortformer_stream(audio, w, cfg: streaming.StreamConfig, steps=None, on_step=None):
+def sortformer_stream(audio, w, cfg: streaming.StreamConfig, steps=None, on_step=None,
+                      live=True):
+    """Streaming Sortformer over a clip delivered live (the end is known only
+    at the final call); ``live=False`` uses the known-length schedule."""
     mel = frontend.log_mel(audio)
     emb = pre_encode_all(w, mel)
+    sched = streaming.live_schedule(len(audio), cfg) if live else None
     return streaming.run_stream(emb, cfg, sortformer_encoder(w), 4, steps=steps,
-                                on_step=on_step)
+                                on_step=on_step, sched=sched)
 
 
 def nemotron_offline(audio, w, cfg: streaming.StreamConfig | None = None, steps=None,

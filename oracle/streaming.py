@@ -14,8 +14,15 @@ scored. NeMo API docs, SortformerStreamingState: the state holds the cache,
 FIFO, their lengths and their predictions.
 
 Readings (pages silent):
-* step s covers encoder frames [sL, min(Te,(s+1)L)); look-ahead is the next
+* known-length schedule (offline chunking, where the clip length is known):
+  step s covers encoder frames [sL, min(Te,(s+1)L)); look-ahead is the next
   min(R, rest) frames, none on the last step;
+* live schedule (streaming, where the end is only known at the final call,
+  as in the Transformers streaming loop that yields full chunks while audio
+  remains and then the rest with is_last_audio_chunk): a non-final step s
+  needs the audio of encoder frames up to (s+1)L+R, i.e. 1280((s+1)L+R)+40
+  samples (the last mel frame's window reaches 40 samples past its frame);
+  the final step scores every remaining frame and has no look-ahead;
 * FIFO predictions are refreshed from every step's window; cache
   predictions are frozen when frames enter the cache;
 * pop rule: when the FIFO exceeds fifo_len, pop
@@ -78,6 +85,27 @@ def schedule(Te: int, cfg: StreamConfig):
         steps.append((c0, c1 - c0, rc, last))
         s += 1
     return steps
+
+
+def live_schedule(n_samples: int, cfg: StreamConfig, hop: int = 160, sub: int = 8):
+    """Schedule of a live stream of n_samples samples: (start, n, rc, last)."""
+    T = n_samples // hop
+    Te = (T + sub - 1) // sub
+    L, R = cfg.chunk_len, cfg.right_context
+    steps = []
+    s = 0
+    while hop * sub * ((s + 1) * L + R) + 40 <= n_samples:
+        steps.append((s * L, L, R, False))
+        s += 1
+    steps.append((s * L, Te - s * L, 0, True))
+    return steps
+
+
+def samples_needed(step: int, cfg: StreamConfig) -> int:
+    """Samples the live stream must have received before non-final step s."""
+    if step == 0:
+        return 1280 * (cfg.chunk_len + cfg.right_context) + 40
+    return 1280 * cfg.chunk_len
 
 
 @dataclasses.dataclass
@@ -194,13 +222,17 @@ def stream_step(state: State, emb_new, n_chunk: int, cfg: StreamConfig, encode, 
 
 
 def run_stream(emb, cfg: StreamConfig, encode, n_spk: int, state: State | None = None,
-               steps=None, on_step=None):
-    """Run the whole schedule over pre-encoded embeddings (Te, D)."""
+               steps=None, on_step=None, sched=None):
+    """Run a schedule (default: known-length) over pre-encoded embeddings (Te, D)."""
     Te, d = emb.shape
     if state is None:
         state = State.empty(d, n_spk)
+    if sched is None:
+        sched = schedule(Te, cfg)
     outs = []
-    for si, (c0, cn, rc, last) in enumerate(schedule(Te, cfg)):
+    for si, (c0, cn, rc, last) in enumerate(sched):
+        if cn == 0:
+            break
         if steps is not None and si >= steps:
             break
         if on_step is not None:

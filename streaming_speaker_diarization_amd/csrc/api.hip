@@ -1,0 +1,536 @@
+// C ABI: argument checks, buffer carving and the streaming state machine.
+// The schedule is host arithmetic only (lengths never depend on device data:
+// compression always leaves exactly spkcache_len frames), so every call just
+// enqueues kernels on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <new>
+
+#include "kernels.h"
+#include "model.h"
+
+using namespace sf;
+using namespace sfm;
+
+namespace {
+
+inline hipStream_t HS(void* s) { return static_cast<hipStream_t>(s); }
+inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline sf_status launched() { return hipGetLastError() == hipSuccess ? SF_OK : SF_EHIP; }
+
+bool valid_stream_config(const sf_stream_config* c) {
+  if (!c) return false;
+  if (c->chunk_len < 1 || c->right_context < 0 || c->fifo_len < 0 || c->update_period < 1 ||
+      c->spkcache_len < 1 || c->n_sil_per_spk < 0)
+    return false;
+  return true;
+}
+
+int stream_cap(const sf_stream_config* c) {
+  return c->spkcache_len + c->fifo_len + c->chunk_len + c->right_context;
+}
+
+long long ring_cap_for(const sf_stream_config* c) {
+  long long need = 1280LL * (c->chunk_len + c->right_context) + 2048, cap = 1;
+  while (cap < need) cap <<= 1;
+  return cap;
+}
+
+// Byte layout of the state buffer.
+struct StateLayout {
+  size_t e, p, ph, sum, cnt, ring, total;
+};
+StateLayout state_layout(const sf_model* m, const sf_stream_config* c, int B) {
+  const size_t cap = stream_cap(c), S = m->cfg.n_spk, D = 512;
+  StateLayout L{};
+  L.e = al256((size_t)B * cap * D * 4);
+  L.p = al256((size_t)B * cap * S * 4);
+  L.ph = al256((size_t)B * cap * 4);
+  L.sum = al256((size_t)B * D * 8);
+  L.cnt = al256((size_t)B * 4);
+  L.ring = al256((size_t)B * ring_cap_for(c) * 4);
+  L.total = 2 * (L.e + L.p + L.ph) + L.sum + L.cnt + L.ring;
+  return L;
+}
+
+void bind_state(sf_stream* st, char* base) {
+  const StateLayout L = state_layout(st->m, &st->sc, st->B);
+  char* p = base;
+  for (int i = 0; i < 2; ++i) {
+    st->E[i] = reinterpret_cast<float*>(p); p += L.e;
+    st->P[i] = reinterpret_cast<float*>(p); p += L.p;
+    st->ph[i] = reinterpret_cast<int*>(p); p += L.ph;
+  }
+  st->sil_sum = reinterpret_cast<double*>(p); p += L.sum;
+  st->sil_cnt = reinterpret_cast<int*>(p); p += L.cnt;
+  st->ring = reinterpret_cast<float*>(p);
+}
+
+void reset_host(sf_stream* st) {
+  st->cur = 0;
+  st->Lc = st->Lf = st->Lp = 0;
+  st->steps = st->emitted = st->recv = 0;
+  st->enc_done = 0;
+  st->finished = false;
+}
+
+void reset_device(sf_stream* st, hipStream_t s) {
+  const long long rows = (long long)st->B * st->cap;
+  fill_i32(st->ph[0], rows, 0, s);
+  fill_i32(st->ph[1], rows, 0, s);
+  fill_f64(st->sil_sum, (long long)st->B * st->D, 0.0, s);
+  fill_i32(st->sil_cnt, st->B, 0, s);
+}
+
+// FIFO refresh/append, pop with silence statistics, compression.
+void state_update(sf_stream* st, const float* probs, int W, int n_chunk, hipStream_t s) {
+  const int S = st->S, D = st->D, B = st->B, cap = st->cap, cur = st->cur;
+  refresh_probs(probs, W, S, B, st->Lc, st->Lf + n_chunk, st->P[cur], st->ph[cur], cap, s);
+  st->Lf += n_chunk;
+  st->Lp -= n_chunk;
+  if (st->Lf > st->sc.fifo_len) {
+    const int np = std::min(st->Lf, std::max(st->sc.update_period, st->Lf - st->sc.fifo_len));
+    silence_update(st->E[cur], st->P[cur], cap, D, S, B, st->Lc, np, st->sil_sum, st->sil_cnt, s);
+    st->Lc += np;
+    st->Lf -= np;
+  }
+  if (st->Lc > st->sc.spkcache_len) {
+    const int C = st->sc.spkcache_len, per = C / S;
+    const int k = std::max(0, per - st->sc.n_sil_per_spk);
+    compress_cache(st->E[cur], st->P[cur], st->ph[cur], cap, D, S, B, st->Lc, st->Lf + st->Lp,
+                   st->sil_sum, st->sil_cnt, C, per, k, st->E[cur ^ 1], st->P[cur ^ 1],
+                   st->ph[cur ^ 1], s);
+    st->cur ^= 1;
+    st->Lc = C;
+  }
+}
+
+// One window forward on the current state, emitting the chunk rows.
+void step_core(sf_stream* st, int n_chunk, float* out, long long out_bstride, EncWs& enc,
+               hipStream_t s) {
+  const sf_model* m = st->m;
+  const int W = st->Lc + st->Lf + st->Lp, S = st->S, B = st->B;
+  copy_rows(st->E[st->cur], (long long)st->cap * st->D, st->D, enc.x, (long long)W * st->D, st->D,
+            B, W, st->D, s);
+  encode(m, enc, B, W, W, s);
+  const int r0 = st->Lc + st->Lf;
+  if (m->cfg.arch == SF_ARCH_SORTFORMER)
+    copy_rows(enc.probs + (size_t)r0 * S, (long long)W * S, S, out, out_bstride, S, B, n_chunk, S, s);
+  else
+    copy_rows(enc.probs10 + (size_t)8 * r0 * S, (long long)8 * W * S, S, out, out_bstride, S, B,
+              8 * n_chunk, S, s);
+  state_update(st, enc.probs, W, n_chunk, s);
+}
+
+size_t stream_ws_bytes(const sf_model* m, const sf_stream_config* c, int B) {
+  return al256(enc_ws_bytes(m, B, stream_cap(c))) +
+         al256(pre_ws_bytes(m, B, c->chunk_len + c->right_context));
+}
+
+int frames_of(long long n_samples) {
+  const long long T = n_samples / 160;
+  return (int)((T + 7) / 8);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sortformer_status_string(sf_status s) {
+  switch (s) {
+    case SF_OK: return "ok";
+    case SF_EINVAL: return "invalid argument";
+    case SF_ESHAPE: return "size outside the supported range";
+    case SF_ENOMEM: return "caller buffer too small";
+    case SF_EHIP: return "HIP runtime error";
+    case SF_ESTATE: return "call not allowed in the current stream state";
+    case SF_EUNSUPPORTED: return "unsupported combination";
+    default: return "unknown status";
+  }
+}
+
+sf_status sortformer_stream_preset(const char* name, sf_stream_config* out) {
+  if (!name || !out) return SF_EINVAL;
+  struct P { const char* n; int v[5]; };
+  static const P presets[] = {{"very_high", {340, 40, 40, 300, 188}},
+                              {"high", {124, 1, 124, 124, 188}},
+                              {"low", {6, 7, 188, 144, 188}},
+                              {"ultra_low", {3, 1, 188, 144, 188}},
+                              {"nemotron_offline", {380, 0, 188, 192, 188}}};
+  for (const P& p : presets)
+    if (std::strcmp(p.n, name) == 0) {
+      *out = sf_stream_config{p.v[0], p.v[1], p.v[2], p.v[3], p.v[4], 3};
+      return SF_OK;
+    }
+  return SF_EINVAL;
+}
+
+size_t sortformer_weight_bytes(const sf_model_config* cfg) { return weight_bytes(cfg); }
+
+sf_status sortformer_init(const sf_model_config* cfg, uint64_t seed, void* d_weights,
+                          size_t bytes, void* stream, sf_model** out) {
+  if (!valid_config(cfg) || !d_weights || !out) return SF_EINVAL;
+  if (reinterpret_cast<uintptr_t>(d_weights) % 256) return SF_EINVAL;
+  if (bytes < weight_bytes(cfg)) return SF_ENOMEM;
+  sf_model* m = new (std::nothrow) sf_model{};
+  if (!m) return SF_ENOMEM;
+  m->cfg = *cfg;
+  m->seed = seed;
+  const sf_status st = init_model(m, d_weights, bytes, HS(stream));
+  if (st != SF_OK) {
+    delete m;
+    return st;
+  }
+  *out = m;
+  return SF_OK;
+}
+
+void sortformer_free(sf_model* m) { delete m; }
+
+sf_status sortformer_get_config(const sf_model* m, sf_model_config* out) {
+  if (!m || !out) return SF_EINVAL;
+  *out = m->cfg;
+  return SF_OK;
+}
+
+int32_t sortformer_num_tensors(const sf_model* m) { return m ? (int32_t)m->list.size() : 0; }
+
+sf_status sortformer_tensor_info(const sf_model* m, int32_t i, char* name, int32_t cap,
+                                 int64_t* numel) {
+  if (!m || i < 0 || i >= (int32_t)m->list.size()) return SF_EINVAL;
+  if (name && cap > 0) {
+    std::strncpy(name, m->list[i].name.c_str(), cap - 1);
+    name[cap - 1] = 0;
+  }
+  if (numel) *numel = m->list[i].numel();
+  return SF_OK;
+}
+
+static void gen_one(const std::vector<sfh::TSpec>& list, uint64_t seed, bool full, int32_t i,
+                    float* out) {
+  std::vector<sfh::TSpec> one(list.size(), sfh::TSpec{"", {0}, 'b'});
+  one[i] = list[i];
+  std::vector<std::vector<float>> w;
+  sfh::generate(one, seed, full, w);
+  std::memcpy(out, w[i].data(), w[i].size() * 4);
+}
+
+sf_status sortformer_get_weights(const sf_model* m, int32_t i, float* host_out) {
+  if (!m || !host_out || i < 0 || i >= (int32_t)m->list.size()) return SF_EINVAL;
+  gen_one(m->list, m->seed, m->cfg.init_mode == SF_INIT_FULL_RANDOM, i, host_out);
+  return SF_OK;
+}
+
+int32_t sortformer_config_num_tensors(const sf_model_config* c) {
+  if (!valid_config(c)) return 0;
+  return (int32_t)(c->arch == SF_ARCH_SORTFORMER ? sfh::sortformer_list(c->n_spk)
+                                                 : sfh::nemotron_list(c->n_spk)).size();
+}
+
+sf_status sortformer_config_tensor(const sf_model_config* c, uint64_t seed, int32_t i, char* name,
+                                   int32_t cap, int64_t* numel, float* host_out) {
+  if (!valid_config(c)) return SF_EINVAL;
+  const auto list = c->arch == SF_ARCH_SORTFORMER ? sfh::sortformer_list(c->n_spk)
+                                                  : sfh::nemotron_list(c->n_spk);
+  if (i < 0 || i >= (int32_t)list.size()) return SF_EINVAL;
+  if (name && cap > 0) {
+    std::strncpy(name, list[i].name.c_str(), cap - 1);
+    name[cap - 1] = 0;
+  }
+  if (numel) *numel = list[i].numel();
+  if (host_out) gen_one(list, seed, c->init_mode == SF_INIT_FULL_RANDOM, i, host_out);
+  return SF_OK;
+}
+
+size_t sortformer_offline_workspace_bytes(const sf_model* m, int32_t B, int64_t N) {
+  if (!m || B < 1 || N < 0) return 0;
+  const int Te = frames_of(N);
+  if (m->cfg.arch == SF_ARCH_SORTFORMER) {
+    if (Te > SF_MAX_WINDOW) return 0;
+    return al256(enc_ws_bytes(m, B, std::max(Te, 1))) + al256(pre_ws_bytes(m, B, Te));
+  }
+  sf_stream_config c{};
+  sortformer_stream_preset("nemotron_offline", &c);
+  return al256(pre_ws_bytes(m, B, Te)) + al256((size_t)B * (Te + 1) * 512 * 4) +
+         al256(state_layout(m, &c, B).total) + al256(enc_ws_bytes(m, B, stream_cap(&c)));
+}
+
+sf_status sortformer_forward_offline(sf_model* m, const float* d_audio, int32_t B, int64_t N,
+                                     float* d_probs, int64_t* n_out, void* d_ws, size_t ws_bytes,
+                                     void* stream) {
+  if (!m || !d_audio || !d_probs || !n_out || !d_ws || B < 1 || N < 0) return SF_EINVAL;
+  const size_t need = sortformer_offline_workspace_bytes(m, B, N);
+  if (need == 0) return SF_ESHAPE;
+  if (ws_bytes < need) return SF_ENOMEM;
+  const hipStream_t s = HS(stream);
+  const int T = (int)(N / 160), Te = frames_of(N), S = m->cfg.n_spk;
+  char* p = static_cast<char*>(d_ws);
+  if (m->cfg.arch == SF_ARCH_SORTFORMER) {
+    *n_out = Te;
+    if (Te == 0) return SF_OK;
+    EncWs enc = carve_enc(m, p, B, Te);
+    char* pre = p + al256(enc_ws_bytes(m, B, Te));
+    pre_encode_range(m, d_audio, N, -1, N, T, 0, Te, B, enc.x, (long long)Te * 512, pre, s);
+    encode(m, enc, B, Te, Te, s);
+    copy_rows(enc.probs, 0, S, d_probs, 0, S, 1, B * Te, S, s);
+    return launched();
+  }
+  // Nemotron-style: 30.4 s chunks with the arrival-order cache and FIFO.
+  *n_out = 8LL * Te;
+  if (Te == 0) return SF_OK;
+  sf_stream st{};
+  st.m = m;
+  sortformer_stream_preset("nemotron_offline", &st.sc);
+  st.B = B; st.S = S; st.D = 512;
+  st.cap = stream_cap(&st.sc);
+  st.ring_cap = ring_cap_for(&st.sc);
+  char* pre = p;
+  p += al256(pre_ws_bytes(m, B, Te));
+  float* emb = reinterpret_cast<float*>(p);
+  p += al256((size_t)B * (Te + 1) * 512 * 4);
+  bind_state(&st, p);
+  p += al256(state_layout(m, &st.sc, B).total);
+  EncWs enc = carve_enc(m, p, B, st.cap);
+  reset_host(&st);
+  reset_device(&st, s);
+  pre_encode_range(m, d_audio, N, -1, N, T, 0, Te, B, emb, (long long)Te * 512, pre, s);
+  const int L = st.sc.chunk_len, R = st.sc.right_context;
+  for (int c0 = 0; c0 < Te; c0 += L) {
+    const int c1 = std::min(Te, c0 + L);
+    const int rc = c1 == Te ? 0 : std::min(R, Te - c1);
+    const int e1 = c1 + rc;
+    copy_rows(emb + (size_t)st.enc_done * 512, (long long)Te * 512, 512,
+              st.E[st.cur] + (size_t)(st.Lc + st.Lf + st.Lp) * 512, (long long)st.cap * 512, 512, B,
+              e1 - st.enc_done, 512, s);
+    st.Lp += e1 - st.enc_done;
+    st.enc_done = e1;
+    step_core(&st, c1 - c0, d_probs + (size_t)8 * c0 * S, (long long)8 * Te * S, enc, s);
+  }
+  return launched();
+}
+
+size_t sortformer_state_bytes(const sf_model* m, const sf_stream_config* c, int32_t B) {
+  if (!m || !valid_stream_config(c) || B < 1 || stream_cap(c) > SF_MAX_WINDOW) return 0;
+  return state_layout(m, c, B).total;
+}
+
+size_t sortformer_stream_workspace_bytes(const sf_model* m, const sf_stream_config* c, int32_t B) {
+  if (!m || !valid_stream_config(c) || B < 1 || stream_cap(c) > SF_MAX_WINDOW) return 0;
+  return stream_ws_bytes(m, c, B);
+}
+
+sf_status sortformer_stream_create(sf_model* m, const sf_stream_config* c, int32_t B,
+                                   void* d_state, size_t bytes, void* stream, sf_stream** out) {
+  if (!m || !valid_stream_config(c) || B < 1 || !d_state || !out) return SF_EINVAL;
+  if (stream_cap(c) > SF_MAX_WINDOW) return SF_ESHAPE;
+  if (c->spkcache_len / m->cfg.n_spk < 1) return SF_ESHAPE;
+  if (reinterpret_cast<uintptr_t>(d_state) % 256) return SF_EINVAL;
+  if (bytes < state_layout(m, c, B).total) return SF_ENOMEM;
+  sf_stream* st = new (std::nothrow) sf_stream{};
+  if (!st) return SF_ENOMEM;
+  st->m = m;
+  st->sc = *c;
+  st->B = B;
+  st->S = m->cfg.n_spk;
+  st->D = 512;
+  st->cap = stream_cap(c);
+  st->ring_cap = ring_cap_for(c);
+  bind_state(st, static_cast<char*>(d_state));
+  reset_host(st);
+  reset_device(st, HS(stream));
+  if (launched() != SF_OK) {
+    delete st;
+    return SF_EHIP;
+  }
+  *out = st;
+  return SF_OK;
+}
+
+void sortformer_stream_destroy(sf_stream* st) { delete st; }
+
+sf_status sortformer_stream_reset(sf_stream* st, void* stream) {
+  if (!st) return SF_EINVAL;
+  reset_host(st);
+  reset_device(st, HS(stream));
+  return launched();
+}
+
+int64_t sortformer_stream_samples_needed(const sf_stream* st) {
+  if (!st) return -1;
+  if (st->finished) return 0;
+  if (st->steps == 0) return 1280LL * (st->sc.chunk_len + st->sc.right_context) + 40;
+  return 1280LL * st->sc.chunk_len;
+}
+
+int32_t sortformer_stream_max_emit(const sf_stream* st) {
+  if (!st) return 0;
+  const int n = st->sc.chunk_len + st->sc.right_context;
+  return st->m->cfg.arch == SF_ARCH_NEMOTRON ? 8 * n : n;
+}
+
+sf_status sortformer_stream_step(sf_stream* st, const float* d_audio_new, int64_t n_new,
+                                 int32_t is_last, float* d_probs_out, int32_t* n_emitted,
+                                 void* d_ws, size_t ws_bytes, void* stream) {
+  if (!st || !n_emitted || !d_ws || !d_probs_out) return SF_EINVAL;
+  if (st->finished) return SF_ESTATE;
+  const long long need = sortformer_stream_samples_needed(st);
+  if (n_new < 0 || n_new > need || (!is_last && n_new != need)) return SF_ESHAPE;
+  if (n_new > 0 && !d_audio_new) return SF_EINVAL;
+  if (ws_bytes < stream_ws_bytes(st->m, &st->sc, st->B)) return SF_ENOMEM;
+  const hipStream_t s = HS(stream);
+  const int L = st->sc.chunk_len, R = st->sc.right_context;
+  const long long N = st->recv + n_new;
+  const int T = (int)(N / 160);
+  const int e1 = is_last ? frames_of(N) : (int)((st->steps + 1) * L + R);
+  const int n_chunk = is_last ? e1 - (int)st->emitted : L;
+  const bool nm = st->m->cfg.arch == SF_ARCH_NEMOTRON;
+  *n_emitted = nm ? 8 * n_chunk : n_chunk;
+  char* p = static_cast<char*>(d_ws);
+  EncWs enc = carve_enc(st->m, p, st->B, st->cap);
+  char* pre = p + al256(enc_ws_bytes(st->m, st->B, st->cap));
+  ring_write(d_audio_new, n_new, st->B, st->ring, st->ring_cap, st->recv, s);
+  pre_encode_range(st->m, st->ring, st->ring_cap, st->ring_cap - 1, N, T, st->enc_done, e1, st->B,
+                   st->E[st->cur] + (size_t)(st->Lc + st->Lf + st->Lp) * st->D,
+                   (long long)st->cap * st->D, pre, s);
+  st->Lp += e1 - st->enc_done;
+  st->enc_done = e1;
+  st->recv = N;
+  if (n_chunk > 0)
+    step_core(st, n_chunk, d_probs_out, (long long)(*n_emitted) * st->S, enc, s);
+  st->steps += 1;
+  st->emitted += n_chunk;
+  st->finished = is_last != 0;
+  return launched();
+}
+
+sf_status sortformer_stream_get_info(const sf_stream* st, int64_t* info, void** ptrs) {
+  if (!st) return SF_EINVAL;
+  if (info) {
+    info[0] = st->Lc; info[1] = st->Lf; info[2] = st->Lp; info[3] = st->cap;
+    info[4] = st->steps; info[5] = st->emitted; info[6] = st->recv; info[7] = st->finished;
+  }
+  if (ptrs) {
+    ptrs[0] = st->E[st->cur]; ptrs[1] = st->P[st->cur]; ptrs[2] = st->ph[st->cur];
+    ptrs[3] = st->sil_sum; ptrs[4] = st->sil_cnt;
+    ptrs[5] = reinterpret_cast<void*>((intptr_t)st->D);
+  }
+  return SF_OK;
+}
+
+static sf_status copy_state(sf_stream* st, bool to_host, float* emb, float* probs, int32_t* flags,
+                            double* sum, int32_t* cnt, hipStream_t s) {
+  const int rows = st->Lc + st->Lf + st->Lp, B = st->B, D = st->D, S = st->S, cur = st->cur;
+  const hipMemcpyKind k = to_host ? hipMemcpyDeviceToHost : hipMemcpyHostToDevice;
+  auto c2 = [&](void* dev, void* host, size_t row_bytes, size_t dev_pitch) -> bool {
+    if (rows == 0 || !host) return true;
+    void* dst = to_host ? host : dev;
+    const void* src = to_host ? dev : host;
+    const size_t dp = to_host ? row_bytes * rows : dev_pitch, sp = to_host ? dev_pitch : row_bytes * rows;
+    return hipMemcpy2DAsync(dst, dp, src, sp, row_bytes * rows, B, k, s) == hipSuccess;
+  };
+  bool ok = c2(st->E[cur], emb, (size_t)D * 4, (size_t)st->cap * D * 4) &&
+            c2(st->P[cur], probs, (size_t)S * 4, (size_t)st->cap * S * 4) &&
+            c2(st->ph[cur], flags, 4, (size_t)st->cap * 4);
+  if (ok && sum)
+    ok = (to_host ? hipMemcpyAsync(sum, st->sil_sum, (size_t)B * D * 8, k, s)
+                  : hipMemcpyAsync(st->sil_sum, sum, (size_t)B * D * 8, k, s)) == hipSuccess;
+  if (ok && cnt)
+    ok = (to_host ? hipMemcpyAsync(cnt, st->sil_cnt, (size_t)B * 4, k, s)
+                  : hipMemcpyAsync(st->sil_cnt, cnt, (size_t)B * 4, k, s)) == hipSuccess;
+  if (!ok || hipStreamSynchronize(s) != hipSuccess) return SF_EHIP;
+  return SF_OK;
+}
+
+sf_status sortformer_stream_export(const sf_stream* st, float* emb, float* probs, int32_t* flags,
+                                   double* sum, int32_t* cnt, void* stream) {
+  if (!st) return SF_EINVAL;
+  return copy_state(const_cast<sf_stream*>(st), true, emb, probs, flags, sum, cnt, HS(stream));
+}
+
+sf_status sortformer_stream_import(sf_stream* st, int32_t Lc, int32_t Lf, int32_t Lp,
+                                   const float* emb, const float* probs, const int32_t* flags,
+                                   const double* sum, const int32_t* cnt, void* stream) {
+  if (!st) return SF_EINVAL;
+  if (Lc < 0 || Lf < 0 || Lp < 0 || Lc > st->sc.spkcache_len || Lf > st->sc.fifo_len ||
+      Lp > st->sc.chunk_len + st->sc.right_context)
+    return SF_ESHAPE;
+  if ((Lc + Lf + Lp > 0) && (!emb || !probs || !flags)) return SF_EINVAL;
+  st->Lc = Lc; st->Lf = Lf; st->Lp = Lp;
+  return copy_state(st, false, const_cast<float*>(emb), const_cast<float*>(probs),
+                    const_cast<int32_t*>(flags), const_cast<double*>(sum),
+                    const_cast<int32_t*>(cnt), HS(stream));
+}
+
+sf_status sortformer_stream_update(sf_stream* st, const float* d_wp, int32_t n_chunk, void* d_ws,
+                                   size_t ws_bytes, void* stream) {
+  if (!st || !d_wp || !d_ws) return SF_EINVAL;
+  if (n_chunk < 0 || n_chunk > st->Lp) return SF_ESHAPE;
+  if (ws_bytes < stream_ws_bytes(st->m, &st->sc, st->B)) return SF_ENOMEM;
+  const hipStream_t s = HS(stream);
+  const int W = st->Lc + st->Lf + st->Lp;
+  EncWs enc = carve_enc(st->m, static_cast<char*>(d_ws), st->B, st->cap);
+  copy_rows(d_wp, 0, st->S, enc.probs, 0, st->S, 1, st->B * W, st->S, s);
+  state_update(st, enc.probs, W, n_chunk, s);
+  return launched();
+}
+
+size_t sortformer_encode_workspace_bytes(const sf_model* m, int32_t B, int32_t W) {
+  if (!m || B < 1 || W < 1 || W > SF_MAX_WINDOW) return 0;
+  return enc_ws_bytes(m, B, W);
+}
+
+sf_status sortformer_encode_window(sf_model* m, const float* d_emb, int32_t B, int32_t W,
+                                   int32_t n_valid, float* d_probs, float* d_probs10, void* d_ws,
+                                   size_t ws_bytes, void* stream) {
+  if (!m || !d_emb || !d_probs || !d_ws) return SF_EINVAL;
+  if (B < 1 || W < 1 || W > SF_MAX_WINDOW || n_valid < 1 || n_valid > W) return SF_ESHAPE;
+  if (ws_bytes < enc_ws_bytes(m, B, W)) return SF_ENOMEM;
+  const hipStream_t s = HS(stream);
+  const int S = m->cfg.n_spk;
+  EncWs enc = carve_enc(m, static_cast<char*>(d_ws), B, W);
+  copy_rows(d_emb, 0, 512, enc.x, 0, 512, 1, B * W, 512, s);
+  encode(m, enc, B, W, n_valid, s);
+  copy_rows(enc.probs, 0, S, d_probs, 0, S, 1, B * W, S, s);
+  if (d_probs10 && m->cfg.arch == SF_ARCH_NEMOTRON)
+    copy_rows(enc.probs10, 0, S, d_probs10, 0, S, 1, B * W * 8, S, s);
+  return launched();
+}
+
+size_t sortformer_pre_encode_workspace_bytes(const sf_model* m, int32_t B, int64_t N) {
+  if (!m || B < 1 || N < 0) return 0;
+  const int Te = frames_of(N);
+  return al256(pre_ws_bytes(m, B, Te)) + al256((size_t)B * (Te + 1) * 512 * 4);
+}
+
+sf_status sortformer_pre_encode(sf_model* m, const float* d_audio, int32_t B, int64_t N,
+                                float* d_mel, float* d_emb, void* d_ws, size_t ws_bytes,
+                                void* stream) {
+  if (!m || !d_audio || !d_ws || B < 1 || N < 0) return SF_EINVAL;
+  const int T = (int)(N / 160), Te = frames_of(N);
+  if (ws_bytes < sortformer_pre_encode_workspace_bytes(m, B, N)) return SF_ENOMEM;
+  if (Te == 0) return SF_OK;
+  const hipStream_t s = HS(stream);
+  char* pre = static_cast<char*>(d_ws);
+  float* emb = reinterpret_cast<float*>(pre + al256(pre_ws_bytes(m, B, Te)));
+  pre_encode_range(m, d_audio, N, -1, N, T, 0, Te, B, emb, (long long)Te * 512, pre, s);
+  if (d_mel) copy_rows(reinterpret_cast<float*>(pre), 0, 128, d_mel, 0, 128, 1, B * T, 128, s);
+  if (d_emb) copy_rows(emb, 0, 512, d_emb, 0, 512, 1, B * Te, 512, s);
+  return launched();
+}
+
+sf_status sortformer_profile_begin(int32_t cls, int32_t max_launches) {
+  if (cls < PROF_GEMM || cls > PROF_CACHE || max_launches < 1) return SF_EINVAL;
+  const int r = prof_start(cls, max_launches);
+  return r == 0 ? SF_OK : (r == -1 ? SF_ESTATE : SF_EHIP);
+}
+
+sf_status sortformer_profile_end(double* ms, int64_t* launches, double* flops, double* bytes) {
+  long long n = 0;
+  const int r = prof_stop(ms, &n, flops, bytes);
+  if (launches) *launches = n;
+  return r == 0 ? SF_OK : (r == -5 ? SF_ESTATE : SF_EHIP);
+}
+
+}  // extern "C"

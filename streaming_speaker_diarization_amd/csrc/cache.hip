@@ -1,0 +1,118 @@
+// Speaker-cache compression ("Streaming Sortformer Diarizer" card, Streaming
+// Architecture: on overflow keep the highest log-odds-scored frames per
+// speaker plus silence placeholders). One workgroup per stream.
+//
+// Score: the log-odds score log p_s - log(1-p_s) + sum_{j!=s} log(1-p_j) is
+// ranked through the monotone-equivalent key
+//   K_s = (p_s/(1-p_s)) * prod_{j!=s, ascending} (1-p_j),  p clamped to [2^-24, 1-2^-24],
+// computed with correctly rounded float64 divide/multiply only (1-p is exact
+// for fp32 p), so the ranking is reproducible bit for bit on any IEEE host.
+// Frames with p_s > 0.5 that are not placeholders are eligible for speaker s;
+// the k largest keys win, ties going to the earlier frame. Block s of the new
+// cache (floor(C/S) slots) holds the winners in time order, then
+// placeholders; trailing slots are placeholders. A placeholder carries the
+// running silence mean (float64 sum / count, rounded to fp32; zero before any
+// silence) and zero probabilities. The rows after the old cache (FIFO and
+// look-ahead) move up behind the new cache.
+// This file is built with floating-point contraction disabled.
+#include "kernels.h"
+
+namespace sf {
+
+#define CMP_MAXM 1024
+#define CMP_MAXS 8
+
+__global__ __launch_bounds__(512) void compress_kernel(const float* E, const float* P,
+                                                       const int* ph, int cap, int D, int S,
+                                                       int M, int tail, const double* sil_sum,
+                                                       const int* sil_cnt, int C, int per, int k,
+                                                       float* E2, float* P2, int* ph2) {
+  __shared__ double keys[CMP_MAXM * CMP_MAXS];   // -1 marks an ineligible (frame, speaker)
+  __shared__ int slot_src[CMP_MAXM];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* Eb = E + (size_t)b * cap * D;
+  const float* Pb = P + (size_t)b * cap * S;
+  const int* phb = ph + (size_t)b * cap;
+
+  for (int idx = tid; idx < M * S; idx += blockDim.x) {
+    const int m = idx / S, s = idx % S;
+    const float ps = Pb[(size_t)m * S + s];
+    double key = -1.0;
+    if (ps > 0.5f && phb[m] == 0) {
+      const double lo = 5.9604644775390625e-8, hi = 1.0 - 5.9604644775390625e-8;
+      double pc = fmin(fmax((double)ps, lo), hi);
+      double kk = pc / (1.0 - pc);
+      for (int j = 0; j < S; ++j) {
+        if (j == s) continue;
+        const double pj = fmin(fmax((double)Pb[(size_t)m * S + j], lo), hi);
+        kk = kk * (1.0 - pj);
+      }
+      key = kk;
+    }
+    keys[idx] = key;
+  }
+  __syncthreads();
+  // Selection: rank among eligible frames of the same speaker.
+  __shared__ unsigned char sel[CMP_MAXM * CMP_MAXS];
+  for (int idx = tid; idx < M * S; idx += blockDim.x) {
+    const int m = idx / S, s = idx % S;
+    const double key = keys[idx];
+    unsigned char chosen = 0;
+    if (key > 0.0) {
+      int rank = 0;
+      for (int q = 0; q < M && rank < k; ++q) {
+        const double kq = keys[q * S + s];
+        rank += (kq > key) || (kq == key && q < m);
+      }
+      chosen = rank < k;
+    }
+    sel[idx] = chosen;
+  }
+  __syncthreads();
+  // Slot assignment: wave s compacts speaker s's winners in frame order.
+  for (int s = wave; s < S; s += blockDim.x / 64) {
+    int base = 0;
+    for (int m0 = 0; m0 < M; m0 += 64) {
+      const int m = m0 + lane;
+      const bool f = m < M && sel[m * S + s];
+      const unsigned long long mask = __ballot(f);
+      const int pos = base + __popcll(mask & ((1ull << lane) - 1ull));
+      if (f) slot_src[s * per + pos] = m;
+      base += __popcll(mask);
+    }
+    for (int r = base + lane; r < per; r += 64) slot_src[s * per + r] = -1;
+  }
+  for (int r = S * per + tid; r < C; r += blockDim.x) slot_src[r] = -1;
+  __syncthreads();
+
+  float* E2b = E2 + (size_t)b * cap * D;
+  float* P2b = P2 + (size_t)b * cap * S;
+  int* ph2b = ph2 + (size_t)b * cap;
+  const int cnt = sil_cnt[b];
+  for (int i = tid; i < C * D; i += blockDim.x) {
+    const int r = i / D, d = i % D, src = slot_src[r];
+    float v;
+    if (src >= 0) v = Eb[(size_t)src * D + d];
+    else v = cnt > 0 ? (float)(sil_sum[(size_t)b * D + d] / (double)cnt) : 0.f;
+    E2b[(size_t)r * D + d] = v;
+  }
+  for (int i = tid; i < C * S; i += blockDim.x) {
+    const int r = i / S, src = slot_src[r];
+    P2b[i] = src >= 0 ? Pb[(size_t)src * S + i % S] : 0.f;
+  }
+  for (int r = tid; r < C; r += blockDim.x) ph2b[r] = slot_src[r] < 0;
+  for (int i = tid; i < tail * D; i += blockDim.x)
+    E2b[(size_t)C * D + i] = Eb[(size_t)M * D + i];
+  for (int i = tid; i < tail * S; i += blockDim.x) P2b[(size_t)C * S + i] = Pb[(size_t)M * S + i];
+  for (int r = tid; r < tail; r += blockDim.x) ph2b[C + r] = phb[M + r];
+}
+
+void compress_cache(const float* E, const float* P, const int* ph, int cap, int D, int S, int B,
+                    int M, int tail, const double* sil_sum, const int* sil_cnt, int C, int per,
+                    int k, float* E2, float* P2, int* ph2, hipStream_t s) {
+  ProfScope ps(PROF_CACHE, s, 0.0, (double)B * ((double)M * (D + S + 1) * 4 + (double)(C + tail) * (D + S + 1) * 4));
+  hipLaunchKernelGGL(compress_kernel, dim3(B), dim3(512), 0, s, E, P, ph, cap, D, S, M, tail,
+                     sil_sum, sil_cnt, C, per, k, E2, P2, ph2);
+}
+
+}  // namespace sf

@@ -1,0 +1,96 @@
+// Launch interfaces of the gfx950 kernels. Every launcher only enqueues on
+// the given stream; shapes are validated by the host code that calls them.
+#pragma once
+#include "common.h"
+
+namespace sf {
+
+enum { EPI_STORE = 0, EPI_SWISH = 1, EPI_RELU = 2, EPI_GELU = 3, EPI_RESID = 4, EPI_GLU = 5 };
+
+struct GemmArgs {
+  const void* A; int lda;   // (M, K) activations
+  const void* W; int ldw;   // (N, K) weights
+  const float* bias;        // (N) or null
+  int M, N, K;
+  void* out; int ldo;       // (M, N) output (EPI_GLU: (M, N/2))
+  int rpb;                  // rows per batch of the output (0: contiguous)
+  long long bstride;        // output elements between batches when rpb != 0
+  float* resid; int ldr;    // EPI_RESID: resid += alpha*y; EPI_STORE: optional fp32 copy
+  float alpha;
+};
+void gemm(const GemmArgs& g, int epi, bool bf16_in, bool bf16_out, hipStream_t s);
+
+enum { ATT_PLAIN = 0, ATT_RELPOS = 1, ATT_ROPE = 2 };
+struct AttnArgs {
+  const void* qkv; int ldq;   // (B*W, ldq) rows, q/k/v column blocks
+  int qoff, koff, voff;
+  int B, H, W, n_valid;
+  const float* ub; const float* vb;   // (H, hd) relative-position biases
+  const void* P; int ldp; int p_center; // relative-position projections, row delta+p_center
+  const float* rope;                  // (max_window, hd/2) (cos, sin) pairs
+  void* ctx; int ldc;                 // (B*W, ldc) output
+  float scale;
+};
+void attention(const AttnArgs& a, int mode, int head_dim, bool bf16, hipStream_t s);
+
+void layernorm(const float* x, int M, int D, const float* g1, const float* b1, const float* g2,
+               const float* b2, float* y_f32, void* y_act, bool bf16, hipStream_t s);
+
+void dwconv_time(const float* glu, int B, int W, int n_valid, const float* w9,
+                 const float* scale, const float* shift, void* out, bool bf16, hipStream_t s);
+
+void logmel(const float* audio, long long a_bstride, long long ring_mask, long long n_total,
+            long long t0, int nfr, int B, const float* tables, float* mel, long long m_bstride,
+            hipStream_t s);
+
+void conv0(const float* mel, long long mel_bstride, int mel_base, int T, float* out,
+           long long out_bstride, int o_base, int n_out, int B, const float* w, const float* b,
+           hipStream_t s);
+void dw2d(const float* in, long long in_bstride, int in_base, int len_in, int f_in, void* out,
+          long long out_bstride, int o_base, int n_out, int B, const float* w, const float* b,
+          bool bf16, hipStream_t s);
+void stack8(const float* mel, long long mel_bstride, int mel_base, int T, int e0, int n, int B,
+            void* out, bool bf16, hipStream_t s);
+
+void head_sortformer(const float* x, int M, const float* w1t, const float* b1, const float* w2,
+                     const float* b2, int S, float* probs, hipStream_t s);
+void head_nemotron(const float* x, int M, const float* hw, const float* hb, const float* uw,
+                   const float* ub, float* p80, float* p10, hipStream_t s);
+
+void copy_rows(const float* src, long long s_bstride, int s_ld, float* dst, long long d_bstride,
+               int d_ld, int B, int rows, int cols, hipStream_t s);
+void ring_write(const float* src, long long n_new, int B, float* ring, long long ring_cap,
+                long long start, hipStream_t s);
+void fill_i32(int* p, long long n, int v, hipStream_t s);
+void fill_f64(double* p, long long n, double v, hipStream_t s);
+void refresh_probs(const float* win_probs, int W, int S, int B, int Lc, int nrows, float* P,
+                   int* ph, int cap, hipStream_t s);
+void silence_update(const float* E, const float* P, int cap, int D, int S, int B, int r0, int n,
+                    double* sil_sum, int* sil_cnt, hipStream_t s);
+void compress_cache(const float* E, const float* P, const int* ph, int cap, int D, int S, int B,
+                    int M, int tail, const double* sil_sum, const int* sil_cnt, int C, int per,
+                    int k, float* E2, float* P2, int* ph2, hipStream_t s);
+
+// Benchmark profiling (see prof.hip). Classes match SF_PROF_* in the ABI.
+enum { PROF_GEMM = 1, PROF_ATTN = 2, PROF_LN = 3, PROF_CONV = 4, PROF_FRONTEND = 5, PROF_CACHE = 6 };
+bool prof_active(int cls);
+void prof_begin_launch(hipStream_t s);
+void prof_end_launch(hipStream_t s, double flops, double bytes);
+int prof_start(int cls, int max_launches);
+int prof_stop(double* ms, long long* launches, double* flops, double* bytes);
+
+// Brackets one launch with profiling events when its class is being profiled.
+struct ProfScope {
+  bool on;
+  hipStream_t s;
+  double f, b;
+  ProfScope(int cls, hipStream_t st, double flops, double bytes)
+      : on(prof_active(cls)), s(st), f(flops), b(bytes) {
+    if (on) prof_begin_launch(s);
+  }
+  ~ProfScope() {
+    if (on) prof_end_launch(s, f, b);
+  }
+};
+
+}  // namespace sf

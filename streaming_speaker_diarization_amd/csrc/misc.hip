@@ -1,0 +1,419 @@
+// Memory-bound kernels of the forward: LayerNorm, the conformer's depthwise
+// time convolution, the log-mel frontend, the strided 2-D convolutions of the
+// 8x subsampling, frame stacking, the speaker heads and the small state
+// copies of the streaming window. All are coalesced along the feature axis.
+#include "kernels.h"
+
+namespace sf {
+
+// ------------------------------------------------------------- LayerNorm
+// One wave per row; statistics in fp32 (two passes over registers).
+// y = LN1(x); optionally z = LN2(y). y_f32 receives the last fp32 result that
+// feeds a residual stream (LN1 if LN2 exists, else LN1), y_act the operand of
+// the next GEMM (LN2 if present, else LN1).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void ln_kernel(const float* x, int M, const float* g1,
+                                                 const float* b1, const float* g2, const float* b2,
+                                                 float* y_f32, T* y_act) {
+  constexpr int PER = D / 64;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= M) return;
+  float v[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) v[i] = x[(size_t)row * D + lane + 64 * i];
+  auto norm = [&](const float* gg, const float* bb) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) s += v[i];
+    const float mean = wave_sum(s) * (1.0f / D);
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) { v[i] -= mean; q += v[i] * v[i]; }
+    const float rstd = 1.0f / sqrtf(wave_sum(q) * (1.0f / D) + 1e-5f);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) v[i] = v[i] * rstd * gg[lane + 64 * i] + bb[lane + 64 * i];
+  };
+  norm(g1, b1);
+  if (y_f32) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) y_f32[(size_t)row * D + lane + 64 * i] = v[i];
+  }
+  if (g2) norm(g2, b2);
+  if (y_act) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) y_act[(size_t)row * D + lane + 64 * i] = from_f<T>(v[i]);
+  }
+}
+
+void layernorm(const float* x, int M, int D, const float* g1, const float* b1, const float* g2,
+               const float* b2, float* y_f32, void* y_act, bool bf16, hipStream_t s) {
+  if (M <= 0) return;
+  ProfScope ps(PROF_LN, s, 0.0,
+               (double)M * D * (4.0 + (y_f32 ? 4.0 : 0.0) + (y_act ? (bf16 ? 2.0 : 4.0) : 0.0)));
+  dim3 grid((M + 3) / 4);
+#define LN_CASE(TT, DD)                                                                      \
+  hipLaunchKernelGGL((ln_kernel<TT, DD>), grid, dim3(256), 0, s, x, M, g1, b1, g2, b2, y_f32, \
+                     static_cast<TT*>(y_act))
+  if (bf16) {
+    if (D == 512) LN_CASE(bf16_t, 512); else LN_CASE(bf16_t, 192);
+  } else {
+    if (D == 512) LN_CASE(float, 512); else LN_CASE(float, 192);
+  }
+#undef LN_CASE
+}
+
+// ------------------------------------------- conformer depthwise conv (k=9)
+// out[t,c] = swish(scale[c] * sum_k w[c,k] g[t+k-4,c] + shift[c]); rows at or
+// beyond n_valid (and outside the window) count as zero. BatchNorm and the
+// conv bias are folded into scale/shift.
+template <typename T>
+__global__ __launch_bounds__(256) void dwconv_time_kernel(const float* glu, int W, int n_valid,
+                                                          const float* w9, const float* sc,
+                                                          const float* sh, T* out) {
+  const int t = blockIdx.x, b = blockIdx.y;
+  const float* gb = glu + (size_t)b * W * 512;
+  for (int c = threadIdx.x; c < 512; c += 256) {
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < 9; ++k) {
+      const int tt = t + k - 4;
+      if (tt >= 0 && tt < n_valid) acc += w9[c * 9 + k] * gb[(size_t)tt * 512 + c];
+    }
+    out[((size_t)b * W + t) * 512 + c] = from_f<T>(swishf_(sc[c] * acc + sh[c]));
+  }
+}
+
+void dwconv_time(const float* glu, int B, int W, int n_valid, const float* w9, const float* sc,
+                 const float* sh, void* out, bool bf16, hipStream_t s) {
+  if (W <= 0) return;
+  ProfScope ps(PROF_CONV, s, 2.0 * 9 * 512 * B * W, (double)B * W * 512 * (4.0 + (bf16 ? 2 : 4)));
+  dim3 grid(W, B);
+  if (bf16)
+    hipLaunchKernelGGL((dwconv_time_kernel<bf16_t>), grid, dim3(256), 0, s, glu, W, n_valid, w9,
+                       sc, sh, static_cast<bf16_t*>(out));
+  else
+    hipLaunchKernelGGL((dwconv_time_kernel<float>), grid, dim3(256), 0, s, glu, W, n_valid, w9, sc,
+                       sh, static_cast<float*>(out));
+}
+
+// ------------------------------------------------------------ log-mel
+// Table block (floats): [0,512) cos(2 pi m/512), [512,1024) sin(2 pi m/512),
+// [1024,1424) analysis window (periodic Hann 400), then per mel band m:
+// lo[m], cnt[m] (as floats) at 1424+2m, and weights at 1680 + m*MELW.
+#define MEL_TAB_LO 1424
+#define MEL_TAB_W 1680
+#define MELW 32
+// Frame t covers samples 160t-200 ... 160t+199 (the non-zero part of the
+// centred 512-point frame); samples outside [0, n_total) are zero. Each
+// workgroup computes 4 frames: |DFT|^2 for 257 bins, then the mel sums and
+// log(x + 2^-24).
+__global__ __launch_bounds__(256) void logmel_kernel(const float* audio, long long a_bstride,
+                                                     long long ring_mask, long long n_total,
+                                                     long long t0, int nfr, const float* tab,
+                                                     float* mel, long long m_bstride) {
+  __shared__ float xs[4][400];
+  __shared__ float tc[512], ts[512];
+  __shared__ float pw[4][257];
+  const int tid = threadIdx.x, b = blockIdx.y, f0 = blockIdx.x * 4;
+  const float* ab = audio + (size_t)b * a_bstride;
+  for (int i = tid; i < 512; i += 256) { tc[i] = tab[i]; ts[i] = tab[512 + i]; }
+  for (int i = tid; i < 4 * 400; i += 256) {
+    const int f = i / 400, n = i % 400;
+    const long long smp = 160 * (t0 + f0 + f) - 200 + n;
+    float v = 0.f;
+    if (f0 + f < nfr && smp >= 0 && smp < n_total) v = ab[smp & ring_mask] * tab[1024 + n];
+    xs[f][n] = v;
+  }
+  __syncthreads();
+  for (int k = tid; k < 257; k += 256) {
+    float re[4] = {0.f, 0.f, 0.f, 0.f}, im[4] = {0.f, 0.f, 0.f, 0.f};
+    int idx = (k * 56) & 511;  // window sample n sits at frame position n+56
+    for (int n = 0; n < 400; ++n) {
+      const float c = tc[idx], s_ = ts[idx];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) { re[f] += xs[f][n] * c; im[f] -= xs[f][n] * s_; }
+      idx = (idx + k) & 511;
+    }
+#pragma unroll
+    for (int f = 0; f < 4; ++f) pw[f][k] = re[f] * re[f] + im[f] * im[f];
+  }
+  __syncthreads();
+  for (int o = tid; o < 4 * 128; o += 256) {
+    const int f = o >> 7, m = o & 127;
+    if (f0 + f >= nfr) continue;
+    const int lo = (int)tab[MEL_TAB_LO + 2 * m], cnt = (int)tab[MEL_TAB_LO + 2 * m + 1];
+    float acc = 0.f;
+    for (int i = 0; i < cnt; ++i) acc += tab[MEL_TAB_W + m * MELW + i] * pw[f][lo + i];
+    mel[(size_t)b * m_bstride + (size_t)(f0 + f) * 128 + m] = logf(acc + 5.9604644775390625e-8f);
+  }
+}
+
+void logmel(const float* audio, long long a_bstride, long long ring_mask, long long n_total,
+            long long t0, int nfr, int B, const float* tab, float* mel, long long m_bstride,
+            hipStream_t s) {
+  if (nfr <= 0) return;
+  ProfScope ps(PROF_FRONTEND, s, (double)B * nfr * (2.0 * 2 * 400 * 257 + 2.0 * 257 * 2),
+               (double)B * nfr * (160 * 4 + 128 * 4));
+  dim3 grid((nfr + 3) / 4, B);
+  hipLaunchKernelGGL(logmel_kernel, grid, dim3(256), 0, s, audio, a_bstride, ring_mask, n_total,
+                     t0, nfr, tab, mel, m_bstride);
+}
+
+// ------------------------------------------------ 8x ConvSubsampling parts
+// Layouts are channels-last: (rows, freq, 256). Row indices are absolute
+// within the utterance; a buffer holds rows [base, base+n). Input rows
+// outside [0, len_in) are the convolution's zero padding.
+__global__ __launch_bounds__(256) void conv0_kernel(const float* mel, long long mel_bstride,
+                                                    int mel_base, int T, float* out,
+                                                    long long out_bstride, int o_base,
+                                                    const float* w, const float* bias) {
+  const int o = blockIdx.x / 64, f = blockIdx.x % 64, b = blockIdx.y, c = threadIdx.x;
+  const float* mb = mel + (size_t)b * mel_bstride;
+  float acc = bias[c];
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    const int r = 2 * (o_base + o) - 1 + a;
+    if (r < 0 || r >= T) continue;
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const int col = 2 * f - 1 + q;
+      if (col < 0 || col >= 128) continue;
+      acc += w[c * 9 + a * 3 + q] * mb[(size_t)(r - mel_base) * 128 + col];
+    }
+  }
+  out[(size_t)b * out_bstride + ((size_t)o * 64 + f) * 256 + c] = fmaxf(acc, 0.f);
+}
+
+void conv0(const float* mel, long long mel_bstride, int mel_base, int T, float* out,
+           long long out_bstride, int o_base, int n_out, int B, const float* w, const float* b,
+           hipStream_t s) {
+  if (n_out <= 0) return;
+  hipLaunchKernelGGL(conv0_kernel, dim3(n_out * 64, B), dim3(256), 0, s, mel, mel_bstride,
+                     mel_base, T, out, out_bstride, o_base, w, b);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void dw2d_kernel(const float* in, long long in_bstride,
+                                                   int in_base, int len_in, int f_in, T* out,
+                                                   long long out_bstride, int o_base,
+                                                   const float* w, const float* bias) {
+  const int f_out = (f_in + 1) / 2;
+  const int o = blockIdx.x / f_out, f = blockIdx.x % f_out, b = blockIdx.y, c = threadIdx.x;
+  const float* ib = in + (size_t)b * in_bstride;
+  float acc = bias[c];
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    const int r = 2 * (o_base + o) - 1 + a;
+    if (r < 0 || r >= len_in) continue;
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const int col = 2 * f - 1 + q;
+      if (col < 0 || col >= f_in) continue;
+      acc += w[c * 9 + a * 3 + q] * ib[((size_t)(r - in_base) * f_in + col) * 256 + c];
+    }
+  }
+  out[(size_t)b * out_bstride + ((size_t)o * f_out + f) * 256 + c] = from_f<T>(acc);
+}
+
+void dw2d(const float* in, long long in_bstride, int in_base, int len_in, int f_in, void* out,
+          long long out_bstride, int o_base, int n_out, int B, const float* w, const float* b,
+          bool bf16, hipStream_t s) {
+  if (n_out <= 0) return;
+  dim3 grid(n_out * ((f_in + 1) / 2), B);
+  if (bf16)
+    hipLaunchKernelGGL((dw2d_kernel<bf16_t>), grid, dim3(256), 0, s, in, in_bstride, in_base,
+                       len_in, f_in, static_cast<bf16_t*>(out), out_bstride, o_base, w, b);
+  else
+    hipLaunchKernelGGL((dw2d_kernel<float>), grid, dim3(256), 0, s, in, in_bstride, in_base, len_in,
+                       f_in, static_cast<float*>(out), out_bstride, o_base, w, b);
+}
+
+// 8x frame stacking: out[b*n + j][r*128 + m] = mel[8(e0+j)+r][m], zero past T.
+template <typename OT>
+__global__ __launch_bounds__(256) void stack8_kernel(const float* mel, long long mel_bstride,
+                                                     int mel_base, int T, int e0, int n, OT* out) {
+  const int j = blockIdx.x, b = blockIdx.y;
+  for (int i = threadIdx.x; i < 1024; i += 256) {
+    const int r = i >> 7, m = i & 127, t = 8 * (e0 + j) + r;
+    const float v = t < T ? mel[(size_t)b * mel_bstride + (size_t)(t - mel_base) * 128 + m] : 0.f;
+    out[((size_t)b * n + j) * 1024 + i] = from_f<OT>(v);
+  }
+}
+
+void stack8(const float* mel, long long mel_bstride, int mel_base, int T, int e0, int n, int B,
+            void* out, bool bf16, hipStream_t s) {
+  if (n <= 0) return;
+  if (bf16)
+    hipLaunchKernelGGL((stack8_kernel<bf16_t>), dim3(n, B), dim3(256), 0, s, mel, mel_bstride,
+                       mel_base, T, e0, n, static_cast<bf16_t*>(out));
+  else
+    hipLaunchKernelGGL((stack8_kernel<float>), dim3(n, B), dim3(256), 0, s, mel, mel_bstride,
+                       mel_base, T, e0, n, static_cast<float*>(out));
+}
+
+// --------------------------------------------------------------- heads
+// Sortformer head, fp32: sigmoid(W2 relu(W1 x + b1) + b2), 8 rows per block.
+__global__ __launch_bounds__(192) void head_sf_kernel(const float* x, int M, const float* w1t,
+                                                      const float* b1, const float* w2,
+                                                      const float* b2, int S, float* probs) {
+  __shared__ float xs[8][192], hs[8][192];
+  const int r0 = blockIdx.x * 8, t = threadIdx.x;
+  for (int r = 0; r < 8; ++r) xs[r][t] = r0 + r < M ? x[(size_t)(r0 + r) * 192 + t] : 0.f;
+  __syncthreads();
+  float acc[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) acc[r] = b1[t];
+  for (int k = 0; k < 192; ++k) {
+    const float wv = w1t[k * 192 + t];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) acc[r] += xs[r][k] * wv;
+  }
+#pragma unroll
+  for (int r = 0; r < 8; ++r) hs[r][t] = fmaxf(acc[r], 0.f);
+  __syncthreads();
+  if (t < 8 * S) {
+    const int r = t / S, sp = t % S;
+    if (r0 + r < M) {
+      float z = b2[sp];
+      for (int k = 0; k < 192; ++k) z += hs[r][k] * w2[sp * 192 + k];
+      probs[(size_t)(r0 + r) * S + sp] = 1.0f / (1.0f + expf(-z));
+    }
+  }
+}
+
+void head_sortformer(const float* x, int M, const float* w1t, const float* b1, const float* w2,
+                     const float* b2, int S, float* probs, hipStream_t s) {
+  if (M <= 0) return;
+  hipLaunchKernelGGL(head_sf_kernel, dim3((M + 7) / 8), dim3(192), 0, s, x, M, w1t, b1, w2, b2, S,
+                     probs);
+}
+
+// Nemotron head, fp32: z = Wh x + bh (80 ms logits), p80 = sigmoid(z);
+// ConvTranspose1d(8,8,k=8,s=8): p10[8t+r][o] = sigmoid(ub[o] + sum_i z[i] uw[i][o][r]).
+__global__ __launch_bounds__(256) void head_nm_kernel(const float* x, int M, const float* hw,
+                                                      const float* hb, const float* uw,
+                                                      const float* ub, float* p80, float* p10) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= M) return;
+  float xv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) xv[i] = x[(size_t)row * 512 + lane + 64 * i];
+  float z[8];
+#pragma unroll
+  for (int sp = 0; sp < 8; ++sp) {
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a += xv[i] * hw[sp * 512 + lane + 64 * i];
+    z[sp] = wave_sum(a) + hb[sp];
+  }
+  if (lane < 8) p80[(size_t)row * 8 + lane] = 1.0f / (1.0f + expf(-z[lane & 7]));
+  const int r = lane >> 3, o = lane & 7;
+  float v = ub[o];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v += z[i] * uw[(i * 8 + o) * 8 + r];
+  p10[((size_t)row * 8 + r) * 8 + o] = 1.0f / (1.0f + expf(-v));
+}
+
+void head_nemotron(const float* x, int M, const float* hw, const float* hb, const float* uw,
+                   const float* ub, float* p80, float* p10, hipStream_t s) {
+  if (M <= 0) return;
+  hipLaunchKernelGGL(head_nm_kernel, dim3((M + 3) / 4), dim3(256), 0, s, x, M, hw, hb, uw, ub,
+                     p80, p10);
+}
+
+// ------------------------------------------------------- state plumbing
+__global__ void copy_rows_kernel(const float* src, long long sb, int sl, float* dst, long long db,
+                                 int dl, int cols) {
+  const int r = blockIdx.x, b = blockIdx.y;
+  const float* sp = src + (size_t)b * sb + (size_t)r * sl;
+  float* dp = dst + (size_t)b * db + (size_t)r * dl;
+  for (int c = threadIdx.x; c < cols; c += blockDim.x) dp[c] = sp[c];
+}
+
+void copy_rows(const float* src, long long sb, int sl, float* dst, long long db, int dl, int B,
+               int rows, int cols, hipStream_t s) {
+  if (rows <= 0 || B <= 0) return;
+  hipLaunchKernelGGL(copy_rows_kernel, dim3(rows, B), dim3(cols >= 256 ? 256 : 64), 0, s, src, sb,
+                     sl, dst, db, dl, cols);
+}
+
+__global__ void ring_write_kernel(const float* src, long long n, float* ring, long long cap,
+                                  long long start) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  const int b = blockIdx.y;
+  if (i < n) ring[(size_t)b * cap + ((start + i) & (cap - 1))] = src[(size_t)b * n + i];
+}
+
+void ring_write(const float* src, long long n, int B, float* ring, long long cap, long long start,
+                hipStream_t s) {
+  if (n <= 0) return;
+  hipLaunchKernelGGL(ring_write_kernel, dim3((unsigned)((n + 255) / 256), B), dim3(256), 0, s, src,
+                     n, ring, cap, start);
+}
+
+__global__ void fill_i32_kernel(int* p, long long n, int v) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+__global__ void fill_f64_kernel(double* p, long long n, double v) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+void fill_i32(int* p, long long n, int v, hipStream_t s) {
+  if (n > 0)
+    hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n, v);
+}
+void fill_f64(double* p, long long n, double v, hipStream_t s) {
+  if (n > 0)
+    hipLaunchKernelGGL(fill_f64_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n, v);
+}
+
+// FIFO prediction refresh and chunk append: state rows [Lc, Lc+nrows) take
+// the window's probabilities at the same rows and are marked real frames.
+__global__ void refresh_kernel(const float* wp, int W, int S, int Lc, int nrows, float* P, int* ph,
+                               int cap) {
+  const int b = blockIdx.x;
+  for (int i = threadIdx.x; i < nrows * S; i += blockDim.x) {
+    const int r = Lc + i / S, sp = i % S;
+    P[((size_t)b * cap + r) * S + sp] = wp[((size_t)b * W + r) * S + sp];
+  }
+  for (int i = threadIdx.x; i < nrows; i += blockDim.x) ph[(size_t)b * cap + Lc + i] = 0;
+}
+
+void refresh_probs(const float* wp, int W, int S, int B, int Lc, int nrows, float* P, int* ph,
+                   int cap, hipStream_t s) {
+  if (nrows <= 0) return;
+  hipLaunchKernelGGL(refresh_kernel, dim3(B), dim3(256), 0, s, wp, W, S, Lc, nrows, P, ph, cap);
+}
+
+// Silence statistics of the frames popped from the FIFO: rows [r0, r0+n) in
+// order; a frame whose largest probability is <= 0.5 adds its embedding to
+// the float64 running sum (one thread per dimension, so the additions happen
+// in frame order) and increments the count.
+__global__ void silence_kernel(const float* E, const float* P, int cap, int D, int S, int r0,
+                               int n, double* sum, int* cnt) {
+  const int b = blockIdx.x;
+  const float* Eb = E + (size_t)b * cap * D;
+  const float* Pb = P + (size_t)b * cap * S;
+  int added = 0;
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    double acc = sum[(size_t)b * D + d];
+    int a = 0;
+    for (int r = r0; r < r0 + n; ++r) {
+      float mx = Pb[(size_t)r * S];
+      for (int sp = 1; sp < S; ++sp) mx = fmaxf(mx, Pb[(size_t)r * S + sp]);
+      if (mx <= 0.5f) { acc += (double)Eb[(size_t)r * D + d]; ++a; }
+    }
+    sum[(size_t)b * D + d] = acc;
+    added = a;
+  }
+  if (threadIdx.x == 0) cnt[b] += added;
+}
+
+void silence_update(const float* E, const float* P, int cap, int D, int S, int B, int r0, int n,
+                    double* sum, int* cnt, hipStream_t s) {
+  if (n <= 0) return;
+  hipLaunchKernelGGL(silence_kernel, dim3(B), dim3(512), 0, s, E, P, cap, D, S, r0, n, sum, cnt);
+}
+
+}  // namespace sf

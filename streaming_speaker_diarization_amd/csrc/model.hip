@@ -1,0 +1,611 @@
+// Model construction (weight arena, derived tables) and the forward graphs:
+// frontend + pre_encode, the Sortformer encoder (17 conformer layers,
+// projection, 18 post-LN transformer layers, speaker head) and the
+// Nemotron-style encoder (31 pre-LN RoPE layers, upsampling head).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+
+#include "host.h"
+#include "kernels.h"
+#include "model.h"
+
+using namespace sf;
+using namespace sfh;
+
+namespace sfm {
+
+// ------------------------------------------------------------------ arena
+namespace {
+struct Arena {
+  size_t off = 0;
+  char* dev = nullptr;   // device base (null while sizing)
+  char* host = nullptr;  // staging copy of the arena (null while sizing)
+  size_t alloc(size_t bytes) {
+    const size_t o = (off + 255) & ~(size_t)255;
+    off = o + bytes;
+    return o;
+  }
+  const float* f32(const float* src, size_t n) {
+    const size_t o = alloc(n * 4);
+    if (host && src) std::memcpy(host + o, src, n * 4);
+    return reinterpret_cast<const float*>(dev + o);
+  }
+  const void* act(const float* src, size_t n, bool bf16) {
+    const size_t o = alloc(n * (bf16 ? 2 : 4));
+    if (host && src) {
+      if (bf16) {
+        uint16_t* d = reinterpret_cast<uint16_t*>(host + o);
+        for (size_t i = 0; i < n; ++i) {
+          uint32_t u;
+          std::memcpy(&u, &src[i], 4);
+          u += 0x7FFFu + ((u >> 16) & 1u);
+          d[i] = (uint16_t)(u >> 16);
+        }
+      } else {
+        std::memcpy(host + o, src, n * 4);
+      }
+    }
+    return dev + o;
+  }
+  void* raw(size_t bytes) { return dev + alloc(bytes); }
+};
+
+struct Src {
+  const std::vector<TSpec>* list;
+  const std::vector<std::vector<float>>* w;  // null while sizing
+  const float* get(const std::string& n) const {
+    if (!w) return nullptr;
+    for (size_t i = 0; i < list->size(); ++i)
+      if ((*list)[i].name == n) return (*w)[i].data();
+    return nullptr;
+  }
+};
+
+// Slaney mel filterbank (128 bands over 0-8 kHz, 257 bins of 31.25 Hz, area
+// normalised), stored sparse: per band the first non-zero bin, the count and
+// the weights.
+double hz2mel(double f) { return f < 1000.0 ? 3.0 * f / 200.0 : 15.0 + 27.0 * std::log(f / 1000.0) / std::log(6.4); }
+double mel2hz(double m) { return m < 15.0 ? 200.0 * m / 3.0 : 1000.0 * std::exp((m - 15.0) * std::log(6.4) / 27.0); }
+
+std::vector<float> frontend_table() {
+  std::vector<float> t(1680 + 128 * 32, 0.f);
+  for (int m = 0; m < 512; ++m) {
+    t[m] = (float)std::cos(2.0 * M_PI * m / 512.0);
+    t[512 + m] = (float)std::sin(2.0 * M_PI * m / 512.0);
+  }
+  for (int n = 0; n < 400; ++n) t[1024 + n] = (float)(0.5 - 0.5 * std::cos(2.0 * M_PI * n / 400.0));
+  double edges[130];
+  const double mmax = hz2mel(8000.0);
+  for (int i = 0; i < 130; ++i) edges[i] = mel2hz(mmax * i / 129.0);
+  for (int m = 0; m < 128; ++m) {
+    const double lo = edges[m], ce = edges[m + 1], hi = edges[m + 2];
+    int first = -1, cnt = 0;
+    for (int k = 0; k <= 256; ++k) {
+      const double f = k * 31.25;
+      const double wv = std::fmax(0.0, std::fmin((f - lo) / (ce - lo), (hi - f) / (hi - ce))) *
+                        (2.0 / (hi - lo));
+      if (wv > 0.0) {
+        if (first < 0) first = k;
+        const int i = k - first;
+        if (i < 32) t[1680 + m * 32 + i] = (float)wv;
+        cnt = i + 1;
+      }
+    }
+    if (first < 0) first = 0;
+    t[1424 + 2 * m] = (float)first;
+    t[1424 + 2 * m + 1] = (float)(cnt > 32 ? 32 : cnt);
+  }
+  return t;
+}
+
+void build_sortformer(sf_model* m, Arena& A, const Src& s) {
+  const bool bf = m->bf16;
+  const bool have = s.w != nullptr;
+  m->c0_w = A.f32(s.get("pre.conv0.w"), 256 * 9);
+  m->c0_b = A.f32(s.get("pre.conv0.b"), 256);
+  for (int k = 0; k < 2; ++k) {
+    const std::string d = "pre.dw" + std::to_string(k + 1), p = "pre.pw" + std::to_string(k + 1);
+    m->dw_w[k] = A.f32(s.get(d + ".w"), 256 * 9);
+    m->dw_b[k] = A.f32(s.get(d + ".b"), 256);
+    m->pw_w[k] = A.act(s.get(p + ".w"), 256 * 256, bf);
+    m->pw_b[k] = A.f32(s.get(p + ".b"), 256);
+  }
+  {  // flatten order: channels-last rows give feature f*256+c; the card's is c*16+f
+    std::vector<float> w;
+    if (have) {
+      const float* src = s.get("pre.out.w");
+      w.resize(512 * 4096);
+      for (int n = 0; n < 512; ++n)
+        for (int c = 0; c < 256; ++c)
+          for (int f = 0; f < 16; ++f) w[(size_t)n * 4096 + f * 256 + c] = src[(size_t)n * 4096 + c * 16 + f];
+    }
+    m->pre_out_w = A.act(have ? w.data() : nullptr, 512 * 4096, bf);
+    m->pre_out_b = A.f32(s.get("pre.out.b"), 512);
+  }
+  for (int l = 0; l < 17; ++l) {
+    const std::string p = "conf" + std::to_string(l) + ".";
+    ConfLayer& L = m->conf[l];
+    L.ff1_g = A.f32(s.get(p + "ff1.ln.g"), 512);
+    L.ff1_b = A.f32(s.get(p + "ff1.ln.b"), 512);
+    L.ff1_w1 = A.act(s.get(p + "ff1.w1"), 2048 * 512, bf);
+    L.ff1_b1 = A.f32(s.get(p + "ff1.b1"), 2048);
+    L.ff1_w2 = A.act(s.get(p + "ff1.w2"), 512 * 2048, bf);
+    L.ff1_b2 = A.f32(s.get(p + "ff1.b2"), 512);
+    L.att_g = A.f32(s.get(p + "att.ln.g"), 512);
+    L.att_b = A.f32(s.get(p + "att.ln.b"), 512);
+    {
+      std::vector<float> w, b;
+      if (have) {
+        w.resize(1536 * 512);
+        b.resize(1536);
+        const char* nm[3] = {"q", "k", "v"};
+        for (int i = 0; i < 3; ++i) {
+          std::memcpy(&w[(size_t)i * 512 * 512], s.get(p + "att.w" + nm[i]), 512 * 512 * 4);
+          std::memcpy(&b[(size_t)i * 512], s.get(p + "att.b" + nm[i]), 512 * 4);
+        }
+      }
+      L.wqkv = A.act(have ? w.data() : nullptr, 1536 * 512, bf);
+      L.bqkv = A.f32(have ? b.data() : nullptr, 1536);
+    }
+    L.wo = A.act(s.get(p + "att.wo"), 512 * 512, bf);
+    L.bo = A.f32(s.get(p + "att.bo"), 512);
+    L.u = A.f32(s.get(p + "att.u"), 512);
+    L.v = A.f32(s.get(p + "att.v"), 512);
+    {  // positional projection, fp32 copy of the (possibly bf16-valued) matrix
+      std::vector<float> w;
+      if (have) {
+        w.assign(s.get(p + "att.wpos"), s.get(p + "att.wpos") + 512 * 512);
+        if (bf)
+          for (auto& x : w) {
+            uint32_t u;
+            std::memcpy(&u, &x, 4);
+            u += 0x7FFFu + ((u >> 16) & 1u);
+            u &= 0xFFFF0000u;
+            std::memcpy(&x, &u, 4);
+          }
+      }
+      L.wpos = const_cast<float*>(A.f32(have ? w.data() : nullptr, 512 * 512));
+    }
+    L.P = A.raw((size_t)(2 * SF_MAX_WINDOW - 1) * 512 * m->esz);
+    L.conv_g = A.f32(s.get(p + "conv.ln.g"), 512);
+    L.conv_b = A.f32(s.get(p + "conv.ln.b"), 512);
+    {  // pointwise-1 rows interleaved in blocks of 16 (value, gate) for the GLU epilogue
+      std::vector<float> w, b;
+      if (have) {
+        w.resize(1024 * 512);
+        b.resize(1024);
+        const float* sw = s.get(p + "conv.pw1.w");
+        const float* sb = s.get(p + "conv.pw1.b");
+        for (int r = 0; r < 1024; ++r) {
+          const int q = r / 32, i = r % 32;
+          const int src = i < 16 ? 16 * q + i : 512 + 16 * q + (i - 16);
+          std::memcpy(&w[(size_t)r * 512], sw + (size_t)src * 512, 512 * 4);
+          b[r] = sb[src];
+        }
+      }
+      L.pw1 = A.act(have ? w.data() : nullptr, 1024 * 512, bf);
+      L.pw1_b = A.f32(have ? b.data() : nullptr, 1024);
+    }
+    L.dw9 = A.f32(s.get(p + "conv.dw.w"), 512 * 9);
+    {  // BatchNorm (eval) and the depthwise bias folded into scale/shift
+      std::vector<float> sc, sh;
+      if (have) {
+        sc.resize(512);
+        sh.resize(512);
+        const float *g = s.get(p + "conv.bn.g"), *bb = s.get(p + "conv.bn.b"),
+                    *mu = s.get(p + "conv.bn.mean"), *var = s.get(p + "conv.bn.var"),
+                    *db = s.get(p + "conv.dw.b");
+        for (int c = 0; c < 512; ++c) {
+          const double k = (double)g[c] / std::sqrt((double)var[c] + 1e-5);
+          sc[c] = (float)k;
+          sh[c] = (float)((double)bb[c] + k * ((double)db[c] - (double)mu[c]));
+        }
+      }
+      L.dw_sc = A.f32(have ? sc.data() : nullptr, 512);
+      L.dw_sh = A.f32(have ? sh.data() : nullptr, 512);
+    }
+    L.pw2 = A.act(s.get(p + "conv.pw2.w"), 512 * 512, bf);
+    L.pw2_b = A.f32(s.get(p + "conv.pw2.b"), 512);
+    L.ff2_g = A.f32(s.get(p + "ff2.ln.g"), 512);
+    L.ff2_b = A.f32(s.get(p + "ff2.ln.b"), 512);
+    L.ff2_w1 = A.act(s.get(p + "ff2.w1"), 2048 * 512, bf);
+    L.ff2_b1 = A.f32(s.get(p + "ff2.b1"), 2048);
+    L.ff2_w2 = A.act(s.get(p + "ff2.w2"), 512 * 2048, bf);
+    L.ff2_b2 = A.f32(s.get(p + "ff2.b2"), 512);
+    L.out_g = A.f32(s.get(p + "out_ln.g"), 512);
+    L.out_b = A.f32(s.get(p + "out_ln.b"), 512);
+  }
+  m->proj_w = A.act(s.get("proj.w"), 192 * 512, bf);
+  m->proj_b = A.f32(s.get("proj.b"), 192);
+  for (int l = 0; l < 18; ++l) {
+    const std::string p = "tf" + std::to_string(l) + ".";
+    TfLayer& L = m->tf[l];
+    std::vector<float> w, b;
+    if (have) {
+      w.resize(576 * 192);
+      b.resize(576);
+      const char* nm[3] = {"q", "k", "v"};
+      for (int i = 0; i < 3; ++i) {
+        std::memcpy(&w[(size_t)i * 192 * 192], s.get(p + "w" + nm[i]), 192 * 192 * 4);
+        std::memcpy(&b[(size_t)i * 192], s.get(p + "b" + nm[i]), 192 * 4);
+      }
+    }
+    L.wqkv = A.act(have ? w.data() : nullptr, 576 * 192, bf);
+    L.bqkv = A.f32(have ? b.data() : nullptr, 576);
+    L.wo = A.act(s.get(p + "wo"), 192 * 192, bf);
+    L.bo = A.f32(s.get(p + "bo"), 192);
+    L.ln1_g = A.f32(s.get(p + "ln1.g"), 192);
+    L.ln1_b = A.f32(s.get(p + "ln1.b"), 192);
+    L.w1 = A.act(s.get(p + "w1"), 768 * 192, bf);
+    L.b1 = A.f32(s.get(p + "b1"), 768);
+    L.w2 = A.act(s.get(p + "w2"), 192 * 768, bf);
+    L.b2 = A.f32(s.get(p + "b2"), 192);
+    L.ln2_g = A.f32(s.get(p + "ln2.g"), 192);
+    L.ln2_b = A.f32(s.get(p + "ln2.b"), 192);
+  }
+  {
+    std::vector<float> w1t;
+    if (have) {
+      w1t.resize(192 * 192);
+      const float* w = s.get("head.w1");
+      for (int n = 0; n < 192; ++n)
+        for (int k = 0; k < 192; ++k) w1t[k * 192 + n] = w[n * 192 + k];
+    }
+    m->h_w1t = A.f32(have ? w1t.data() : nullptr, 192 * 192);
+    m->h_b1 = A.f32(s.get("head.b1"), 192);
+    m->h_w2 = A.f32(s.get("head.w2"), (size_t)m->cfg.n_spk * 192);
+    m->h_b2 = A.f32(s.get("head.b2"), m->cfg.n_spk);
+  }
+  {  // interleaved sinusoids for relative distances -(Wmax-1) .. Wmax-1
+    std::vector<float> pe;
+    if (have) {
+      pe.resize((size_t)(2 * SF_MAX_WINDOW - 1) * 512);
+      for (int r = 0; r < 2 * SF_MAX_WINDOW - 1; ++r) {
+        const double delta = r - (SF_MAX_WINDOW - 1);
+        for (int k = 0; k < 256; ++k) {
+          const double om = std::pow(10000.0, -2.0 * k / 512.0);
+          pe[(size_t)r * 512 + 2 * k] = (float)std::sin(delta * om);
+          pe[(size_t)r * 512 + 2 * k + 1] = (float)std::cos(delta * om);
+        }
+      }
+    }
+    m->pe = const_cast<float*>(A.f32(have ? pe.data() : nullptr, (size_t)(2 * SF_MAX_WINDOW - 1) * 512));
+  }
+}
+
+void build_nemotron(sf_model* m, Arena& A, const Src& s) {
+  const bool bf = m->bf16;
+  const bool have = s.w != nullptr;
+  m->in_w = A.act(s.get("in.w"), 512 * 1024, bf);
+  m->in_b = A.f32(s.get("in.b"), 512);
+  for (int l = 0; l < 31; ++l) {
+    const std::string p = "rl" + std::to_string(l) + ".";
+    TfLayer& L = m->rl[l];
+    L.ln1_g = A.f32(s.get(p + "ln1.g"), 512);
+    L.ln1_b = A.f32(s.get(p + "ln1.b"), 512);
+    std::vector<float> w, b;
+    if (have) {
+      w.resize(1536 * 512);
+      b.resize(1536);
+      const char* nm[3] = {"q", "k", "v"};
+      for (int i = 0; i < 3; ++i) {
+        std::memcpy(&w[(size_t)i * 512 * 512], s.get(p + "w" + nm[i]), 512 * 512 * 4);
+        std::memcpy(&b[(size_t)i * 512], s.get(p + "b" + nm[i]), 512 * 4);
+      }
+    }
+    L.wqkv = A.act(have ? w.data() : nullptr, 1536 * 512, bf);
+    L.bqkv = A.f32(have ? b.data() : nullptr, 1536);
+    L.wo = A.act(s.get(p + "wo"), 512 * 512, bf);
+    L.bo = A.f32(s.get(p + "bo"), 512);
+    L.ln2_g = A.f32(s.get(p + "ln2.g"), 512);
+    L.ln2_b = A.f32(s.get(p + "ln2.b"), 512);
+    L.w1 = A.act(s.get(p + "w1"), 2048 * 512, bf);
+    L.b1 = A.f32(s.get(p + "b1"), 2048);
+    L.w2 = A.act(s.get(p + "w2"), 512 * 2048, bf);
+    L.b2 = A.f32(s.get(p + "b2"), 512);
+  }
+  m->fin_g = A.f32(s.get("final_ln.g"), 512);
+  m->fin_b = A.f32(s.get("final_ln.b"), 512);
+  m->nh_w = A.f32(s.get("head.w"), 8 * 512);
+  m->nh_b = A.f32(s.get("head.b"), 8);
+  m->up_w = A.f32(s.get("up.w"), 8 * 8 * 8);
+  m->up_b = A.f32(s.get("up.b"), 8);
+  std::vector<float> rope;
+  if (have) {  // rotate-half tables: angle = pos * 10000^(-i/32), i < 32
+    rope.resize((size_t)SF_MAX_WINDOW * 64);
+    for (int pos = 0; pos < SF_MAX_WINDOW; ++pos)
+      for (int i = 0; i < 32; ++i) {
+        const double ang = pos * std::pow(10000.0, -(double)i / 32.0);
+        rope[((size_t)pos * 32 + i) * 2] = (float)std::cos(ang);
+        rope[((size_t)pos * 32 + i) * 2 + 1] = (float)std::sin(ang);
+      }
+  }
+  m->rope = A.f32(have ? rope.data() : nullptr, (size_t)SF_MAX_WINDOW * 64);
+}
+
+void build(sf_model* m, Arena& A, const Src& s) {
+  if (m->cfg.arch == SF_ARCH_SORTFORMER) build_sortformer(m, A, s);
+  else build_nemotron(m, A, s);
+  std::vector<float> tab;
+  if (s.w) tab = frontend_table();
+  m->fe_tab = A.f32(s.w ? tab.data() : nullptr, 1680 + 128 * 32);
+}
+}  // namespace
+
+bool valid_config(const sf_model_config* c) {
+  if (!c) return false;
+  if (c->arch != SF_ARCH_SORTFORMER && c->arch != SF_ARCH_NEMOTRON) return false;
+  if (c->dtype != SF_DTYPE_F32 && c->dtype != SF_DTYPE_BF16) return false;
+  if (c->init_mode != SF_INIT_SPEC && c->init_mode != SF_INIT_FULL_RANDOM) return false;
+  if (c->arch == SF_ARCH_SORTFORMER && c->n_spk != 4) return false;
+  if (c->arch == SF_ARCH_NEMOTRON && c->n_spk != 8) return false;
+  return true;
+}
+
+size_t weight_bytes(const sf_model_config* c) {
+  if (!valid_config(c)) return 0;
+  sf_model tmp{};
+  tmp.cfg = *c;
+  tmp.bf16 = c->dtype == SF_DTYPE_BF16;
+  tmp.esz = tmp.bf16 ? 2 : 4;
+  tmp.list = c->arch == SF_ARCH_SORTFORMER ? sortformer_list(c->n_spk) : nemotron_list(c->n_spk);
+  Arena A;
+  build(&tmp, A, Src{&tmp.list, nullptr});
+  return (A.off + 255) & ~(size_t)255;
+}
+
+sf_status init_model(sf_model* m, void* d_weights, size_t bytes, hipStream_t st) {
+  m->bf16 = m->cfg.dtype == SF_DTYPE_BF16;
+  m->esz = m->bf16 ? 2 : 4;
+  m->list = m->cfg.arch == SF_ARCH_SORTFORMER ? sortformer_list(m->cfg.n_spk)
+                                              : nemotron_list(m->cfg.n_spk);
+  std::vector<std::vector<float>> w;
+  generate(m->list, m->seed, m->cfg.init_mode == SF_INIT_FULL_RANDOM, w);
+  const size_t need = weight_bytes(&m->cfg);
+  if (bytes < need) return SF_ENOMEM;
+  std::vector<char> host(need, 0);
+  Arena A;
+  A.dev = static_cast<char*>(d_weights);
+  A.host = host.data();
+  build(m, A, Src{&m->list, &w});
+  m->base = static_cast<char*>(d_weights);
+  m->bytes = need;
+  if (hipMemcpyAsync(d_weights, host.data(), need, hipMemcpyHostToDevice, st) != hipSuccess)
+    return SF_EHIP;
+  if (m->cfg.arch == SF_ARCH_SORTFORMER) {
+    // p(delta) = W_pos pe(delta) for every representable delta, per layer
+    for (int l = 0; l < 17; ++l) {
+      GemmArgs g{};
+      g.A = m->pe; g.lda = 512;
+      g.W = m->conf[l].wpos; g.ldw = 512;
+      g.bias = nullptr;
+      g.M = 2 * SF_MAX_WINDOW - 1; g.N = 512; g.K = 512;
+      g.out = m->conf[l].P; g.ldo = 512;
+      gemm(g, EPI_STORE, false, m->bf16, st);
+    }
+  }
+  if (hipStreamSynchronize(st) != hipSuccess) return SF_EHIP;
+  if (hipGetLastError() != hipSuccess) return SF_EHIP;
+  return SF_OK;
+}
+
+// ---------------------------------------------------------- workspaces
+size_t enc_ws_bytes(const sf_model* m, int B, int W) {
+  const size_t r = (size_t)B * W, es = m->esz;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  size_t t = 0;
+  t += al(r * 512 * 4);   // x
+  t += al(r * 512 * es);  // h
+  t += al(r * 2048 * es); // big
+  t += al(r * 512 * es);  // ctx
+  t += al(r * 512 * 4);   // glu
+  t += al(r * 8 * 4);     // probs
+  t += al(r * 64 * 4);    // probs10
+  return t;
+}
+
+EncWs carve_enc(const sf_model* m, char* p, int B, int W) {
+  const size_t r = (size_t)B * W, es = m->esz;
+  auto take = [&](size_t bytes) {
+    char* q = p;
+    p += (bytes + 255) & ~(size_t)255;
+    return q;
+  };
+  EncWs w;
+  w.x = reinterpret_cast<float*>(take(r * 512 * 4));
+  w.h = take(r * 512 * es);
+  w.big = take(r * 2048 * es);
+  w.ctx = take(r * 512 * es);
+  w.glu = reinterpret_cast<float*>(take(r * 512 * 4));
+  w.probs = reinterpret_cast<float*>(take(r * 8 * 4));
+  w.probs10 = reinterpret_cast<float*>(take(r * 64 * 4));
+  return w;
+}
+
+size_t pre_ws_bytes(const sf_model* m, int B, int n) {
+  const size_t es = m->esz, b = B, nn = n + 1;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  size_t t = al(b * (8 * nn) * 128 * 4);  // mel
+  if (m->cfg.arch == SF_ARCH_SORTFORMER) {
+    t += al(b * (4 * nn) * 64 * 256 * 4);  // conv0 out
+    t += al(b * (2 * nn) * 32 * 256 * es); // dw1 out
+    t += al(b * (2 * nn) * 32 * 256 * 4);  // pw1 out
+    t += al(b * nn * 16 * 256 * es);       // dw2 out
+    t += al(b * nn * 16 * 256 * es);       // pw2 out
+  } else {
+    t += al(b * nn * 1024 * es);           // stacked frames
+  }
+  return t;
+}
+
+// Encoder frames [e0, e1) of every stream from audio. Audio sample s of
+// stream b is audio[b*a_bstride + (s & ring_mask)]; samples >= n_total are
+// zero. T = mel frames of the utterance known so far. Output rows go to
+// dst + b*dst_bstride + (j-e0)*512 (fp32).
+void pre_encode_range(const sf_model* m, const float* audio, long long a_bstride,
+                      long long ring_mask, long long n_total, int T, int e0, int e1, int B,
+                      float* dst, long long dst_bstride, char* wsp, hipStream_t s) {
+  const int n = e1 - e0;
+  if (n <= 0) return;
+  const bool bf = m->bf16;
+  const size_t es = m->esz;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  char* p = wsp;
+  const size_t nn = n + 1;
+  float* mel = reinterpret_cast<float*>(p);
+  p += al((size_t)B * 8 * nn * 128 * 4);
+  if (m->cfg.arch == SF_ARCH_SORTFORMER) {
+    const int T1 = (T + 1) / 2, T2 = (T1 + 1) / 2;
+    const int t0 = std::max(0, 8 * e0 - 8), t1 = std::min(T, 8 * e1);
+    const int a1 = std::max(0, 4 * e0 - 3), b1 = std::min(T1, 4 * e1);
+    const int a2 = std::max(0, 2 * e0 - 1), b2 = std::min(T2, 2 * e1);
+    float* l1 = reinterpret_cast<float*>(p);
+    p += al((size_t)B * 4 * nn * 64 * 256 * 4);
+    void* d1 = p;
+    p += al((size_t)B * 2 * nn * 32 * 256 * es);
+    float* p1 = reinterpret_cast<float*>(p);
+    p += al((size_t)B * 2 * nn * 32 * 256 * 4);
+    void* d2 = p;
+    p += al((size_t)B * nn * 16 * 256 * es);
+    void* p2 = p;
+    const long long mel_bs = (long long)(t1 - t0) * 128;
+    logmel(audio, a_bstride, ring_mask, n_total, t0, t1 - t0, B, m->fe_tab, mel, mel_bs, s);
+    const long long l1_bs = (long long)(b1 - a1) * 64 * 256;
+    conv0(mel, mel_bs, t0, T, l1, l1_bs, a1, b1 - a1, B, m->c0_w, m->c0_b, s);
+    const long long d1_bs = (long long)(b2 - a2) * 32 * 256;
+    dw2d(l1, l1_bs, a1, T1, 64, d1, d1_bs, a2, b2 - a2, B, m->dw_w[0], m->dw_b[0], bf, s);
+    GemmArgs g{};
+    g.A = d1; g.lda = 256; g.W = m->pw_w[0]; g.ldw = 256; g.bias = m->pw_b[0];
+    g.M = B * (b2 - a2) * 32; g.N = 256; g.K = 256; g.out = p1; g.ldo = 256;
+    gemm(g, EPI_RELU, bf, false, s);
+    const long long d2_bs = (long long)n * 16 * 256;
+    dw2d(p1, d1_bs, a2, T2, 32, d2, d2_bs, e0, n, B, m->dw_w[1], m->dw_b[1], bf, s);
+    g = GemmArgs{};
+    g.A = d2; g.lda = 256; g.W = m->pw_w[1]; g.ldw = 256; g.bias = m->pw_b[1];
+    g.M = B * n * 16; g.N = 256; g.K = 256; g.out = p2; g.ldo = 256;
+    gemm(g, EPI_RELU, bf, bf, s);
+    g = GemmArgs{};
+    g.A = p2; g.lda = 4096; g.W = m->pre_out_w; g.ldw = 4096; g.bias = m->pre_out_b;
+    g.M = B * n; g.N = 512; g.K = 4096; g.out = dst; g.ldo = 512; g.rpb = n; g.bstride = dst_bstride;
+    gemm(g, EPI_STORE, bf, false, s);
+  } else {
+    const int t0 = 8 * e0, t1 = std::min(T, 8 * e1);
+    void* st = p;
+    const long long mel_bs = (long long)std::max(0, t1 - t0) * 128;
+    logmel(audio, a_bstride, ring_mask, n_total, t0, t1 - t0, B, m->fe_tab, mel, mel_bs, s);
+    stack8(mel, mel_bs, t0, T, e0, n, B, st, bf, s);
+    GemmArgs g{};
+    g.A = st; g.lda = 1024; g.W = m->in_w; g.ldw = 1024; g.bias = m->in_b;
+    g.M = B * n; g.N = 512; g.K = 1024; g.out = dst; g.ldo = 512; g.rpb = n; g.bstride = dst_bstride;
+    gemm(g, EPI_STORE, bf, false, s);
+  }
+}
+
+// ------------------------------------------------------------- encoders
+static void gemm_(const void* A, int lda, const void* W, int ldw, const float* bias, int M, int N,
+                  int K, void* out, int ldo, int epi, bool bf_in, bool bf_out, hipStream_t s,
+                  float* resid = nullptr, int ldr = 0, float alpha = 1.f) {
+  GemmArgs g{};
+  g.A = A; g.lda = lda; g.W = W; g.ldw = ldw; g.bias = bias; g.M = M; g.N = N; g.K = K;
+  g.out = out; g.ldo = ldo; g.resid = resid; g.ldr = ldr; g.alpha = alpha;
+  gemm(g, epi, bf_in, bf_out, s);
+}
+
+static void encode_sortformer(const sf_model* m, EncWs& w, int B, int W, int n_valid,
+                              hipStream_t s) {
+  const bool bf = m->bf16;
+  const int M = B * W;
+  float* x = w.x;
+  layernorm(x, M, 512, m->conf[0].ff1_g, m->conf[0].ff1_b, nullptr, nullptr, nullptr, w.h, bf, s);
+  for (int l = 0; l < 17; ++l) {
+    const ConfLayer& L = m->conf[l];
+    // macaron FFN, first half
+    gemm_(w.h, 512, L.ff1_w1, 512, L.ff1_b1, M, 2048, 512, w.big, 2048, EPI_SWISH, bf, bf, s);
+    gemm_(w.big, 2048, L.ff1_w2, 2048, L.ff1_b2, M, 512, 2048, nullptr, 0, EPI_RESID, bf, false, s,
+          x, 512, 0.5f);
+    // relative-position self-attention
+    layernorm(x, M, 512, L.att_g, L.att_b, nullptr, nullptr, nullptr, w.h, bf, s);
+    gemm_(w.h, 512, L.wqkv, 512, L.bqkv, M, 1536, 512, w.big, 1536, EPI_STORE, bf, bf, s);
+    AttnArgs a{};
+    a.qkv = w.big; a.ldq = 1536; a.qoff = 0; a.koff = 512; a.voff = 1024;
+    a.B = B; a.H = 8; a.W = W; a.n_valid = n_valid;
+    a.ub = L.u; a.vb = L.v; a.P = L.P; a.ldp = 512; a.p_center = SF_MAX_WINDOW - 1;
+    a.ctx = w.ctx; a.ldc = 512; a.scale = 0.125f;
+    attention(a, ATT_RELPOS, 64, bf, s);
+    gemm_(w.ctx, 512, L.wo, 512, L.bo, M, 512, 512, nullptr, 0, EPI_RESID, bf, false, s, x, 512,
+          1.f);
+    // convolution module
+    layernorm(x, M, 512, L.conv_g, L.conv_b, nullptr, nullptr, nullptr, w.h, bf, s);
+    gemm_(w.h, 512, L.pw1, 512, L.pw1_b, M, 1024, 512, w.glu, 512, EPI_GLU, bf, false, s);
+    dwconv_time(w.glu, B, W, n_valid, L.dw9, L.dw_sc, L.dw_sh, w.h, bf, s);
+    gemm_(w.h, 512, L.pw2, 512, L.pw2_b, M, 512, 512, nullptr, 0, EPI_RESID, bf, false, s, x, 512,
+          1.f);
+    // macaron FFN, second half
+    layernorm(x, M, 512, L.ff2_g, L.ff2_b, nullptr, nullptr, nullptr, w.h, bf, s);
+    gemm_(w.h, 512, L.ff2_w1, 512, L.ff2_b1, M, 2048, 512, w.big, 2048, EPI_SWISH, bf, bf, s);
+    gemm_(w.big, 2048, L.ff2_w2, 2048, L.ff2_b2, M, 512, 2048, nullptr, 0, EPI_RESID, bf, false, s,
+          x, 512, 0.5f);
+    // output LayerNorm (fused with the next layer's first LayerNorm)
+    if (l < 16)
+      layernorm(x, M, 512, L.out_g, L.out_b, m->conf[l + 1].ff1_g, m->conf[l + 1].ff1_b, x, w.h,
+                bf, s);
+    else
+      layernorm(x, M, 512, L.out_g, L.out_b, nullptr, nullptr, nullptr, w.h, bf, s);
+  }
+  // encoder_proj: fp32 residual stream for the transformer + GEMM operand
+  gemm_(w.h, 512, m->proj_w, 512, m->proj_b, M, 192, 512, w.ctx, 192, EPI_STORE, bf, bf, s, x,
+        192);
+  const void* hin = w.ctx;
+  for (int l = 0; l < 18; ++l) {
+    const TfLayer& L = m->tf[l];
+    gemm_(hin, 192, L.wqkv, 192, L.bqkv, M, 576, 192, w.big, 576, EPI_STORE, bf, bf, s);
+    AttnArgs a{};
+    a.qkv = w.big; a.ldq = 576; a.qoff = 0; a.koff = 192; a.voff = 384;
+    a.B = B; a.H = 8; a.W = W; a.n_valid = n_valid;
+    a.ctx = w.ctx; a.ldc = 192; a.scale = 1.0f / std::sqrt(24.0f);
+    attention(a, ATT_PLAIN, 24, bf, s);
+    gemm_(w.ctx, 192, L.wo, 192, L.bo, M, 192, 192, nullptr, 0, EPI_RESID, bf, false, s, x, 192,
+          1.f);
+    layernorm(x, M, 192, L.ln1_g, L.ln1_b, nullptr, nullptr, x, w.h, bf, s);
+    gemm_(w.h, 192, L.w1, 192, L.b1, M, 768, 192, w.big, 768, EPI_RELU, bf, bf, s);
+    gemm_(w.big, 768, L.w2, 768, L.b2, M, 192, 768, nullptr, 0, EPI_RESID, bf, false, s, x, 192,
+          1.f);
+    layernorm(x, M, 192, L.ln2_g, L.ln2_b, nullptr, nullptr, x, w.h, bf, s);
+    hin = w.h;
+  }
+  head_sortformer(x, M, m->h_w1t, m->h_b1, m->h_w2, m->h_b2, m->cfg.n_spk, w.probs, s);
+}
+
+static void encode_nemotron(const sf_model* m, EncWs& w, int B, int W, int n_valid,
+                            hipStream_t s) {
+  const bool bf = m->bf16;
+  const int M = B * W;
+  float* x = w.x;
+  for (int l = 0; l < 31; ++l) {
+    const TfLayer& L = m->rl[l];
+    layernorm(x, M, 512, L.ln1_g, L.ln1_b, nullptr, nullptr, nullptr, w.h, bf, s);
+    gemm_(w.h, 512, L.wqkv, 512, L.bqkv, M, 1536, 512, w.big, 1536, EPI_STORE, bf, bf, s);
+    AttnArgs a{};
+    a.qkv = w.big; a.ldq = 1536; a.qoff = 0; a.koff = 512; a.voff = 1024;
+    a.B = B; a.H = 8; a.W = W; a.n_valid = n_valid; a.rope = m->rope;
+    a.ctx = w.ctx; a.ldc = 512; a.scale = 0.125f;
+    attention(a, ATT_ROPE, 64, bf, s);
+    gemm_(w.ctx, 512, L.wo, 512, L.bo, M, 512, 512, nullptr, 0, EPI_RESID, bf, false, s, x, 512,
+          1.f);
+    layernorm(x, M, 512, L.ln2_g, L.ln2_b, nullptr, nullptr, nullptr, w.h, bf, s);
+    gemm_(w.h, 512, L.w1, 512, L.b1, M, 2048, 512, w.big, 2048, EPI_GELU, bf, bf, s);
+    gemm_(w.big, 2048, L.w2, 2048, L.b2, M, 512, 2048, nullptr, 0, EPI_RESID, bf, false, s, x, 512,
+          1.f);
+  }
+  layernorm(x, M, 512, m->fin_g, m->fin_b, nullptr, nullptr, x, nullptr, bf, s);
+  head_nemotron(x, M, m->nh_w, m->nh_b, m->up_w, m->up_b, w.probs, w.probs10, s);
+}
+
+void encode(const sf_model* m, EncWs& w, int B, int W, int n_valid, hipStream_t s) {
+  if (m->cfg.arch == SF_ARCH_SORTFORMER) encode_sortformer(m, w, B, W, n_valid, s);
+  else encode_nemotron(m, w, B, W, n_valid, s);
+}
+
+}  // namespace sfm

@@ -1,0 +1,79 @@
+// Per-kernel-class timing for benchmarks. While a class is being profiled,
+// every launch of that class is bracketed by a pair of HIP events recorded on
+// the launch's own stream, and the launch's algorithmic flop and byte counts
+// are accumulated (what the operation must compute and move, independent of
+// how the kernel tiles it).
+#include <vector>
+
+#include "kernels.h"
+
+namespace sf {
+
+namespace {
+struct Prof {
+  bool on = false;
+  int cls = 0;
+  std::vector<hipEvent_t> ev;
+  size_t used = 0;
+  double flops = 0, bytes = 0;
+  long long launches = 0;
+};
+Prof& P() {
+  static Prof p;
+  return p;
+}
+}  // namespace
+
+bool prof_active(int cls) {
+  Prof& p = P();
+  return p.on && p.cls == cls && p.used + 2 <= p.ev.size();
+}
+
+void prof_begin_launch(hipStream_t s) {
+  Prof& p = P();
+  hipEventRecord(p.ev[p.used], s);
+}
+
+void prof_end_launch(hipStream_t s, double flops, double bytes) {
+  Prof& p = P();
+  hipEventRecord(p.ev[p.used + 1], s);
+  p.used += 2;
+  p.flops += flops;
+  p.bytes += bytes;
+  p.launches += 1;
+}
+
+int prof_start(int cls, int max_launches) {
+  Prof& p = P();
+  if (p.on || max_launches < 1) return -1;
+  for (auto e : p.ev) hipEventDestroy(e);
+  p.ev.assign((size_t)2 * max_launches, nullptr);
+  for (auto& e : p.ev)
+    if (hipEventCreate(&e) != hipSuccess) return -4;
+  p.used = 0;
+  p.flops = p.bytes = 0;
+  p.launches = 0;
+  p.cls = cls;
+  p.on = true;
+  return 0;
+}
+
+int prof_stop(double* ms, long long* launches, double* flops, double* bytes) {
+  Prof& p = P();
+  if (!p.on) return -5;
+  p.on = false;
+  double total = 0;
+  for (size_t i = 0; i < p.used; i += 2) {
+    if (hipEventSynchronize(p.ev[i + 1]) != hipSuccess) return -4;
+    float t = 0;
+    if (hipEventElapsedTime(&t, p.ev[i], p.ev[i + 1]) != hipSuccess) return -4;
+    total += t;
+  }
+  if (ms) *ms = total;
+  if (launches) *launches = p.launches;
+  if (flops) *flops = p.flops;
+  if (bytes) *bytes = p.bytes;
+  return 0;
+}
+
+}  // namespace sf

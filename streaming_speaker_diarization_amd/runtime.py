@@ -1,0 +1,125 @@
+"""Buffer management around the C ABI: allocates the weight, workspace and
+state buffers with PyTorch on the current device and calls the library.
+No arithmetic of the method happens here."""
+from __future__ import annotations
+
+import torch
+
+from . import sortformer as sf
+
+
+def _bytes(n: int, device) -> torch.Tensor:
+    return torch.empty(max(int(n), 1), dtype=torch.uint8, device=device)
+
+
+class Model:
+    def __init__(self, arch: str = "sortformer", dtype: str = "bf16", seed: int | None = None,
+                 full_random: bool = False, device: str = "cuda"):
+        if not torch.cuda.is_available():
+            raise RuntimeError("the HIP library needs a GPU")
+        self.arch, self.dtype = arch, dtype
+        self.cfg = sf.model_config(arch, dtype, full_random)
+        self.seed = (0 if arch == "sortformer" else 1) if seed is None else seed
+        self.device = torch.device(device)
+        nbytes = sf.sortformer_weight_bytes(self.cfg)
+        if nbytes == 0:
+            raise ValueError("invalid model configuration")
+        self.weights = _bytes(nbytes, self.device)
+        self.handle = sf.sortformer_init(self.cfg, self.seed, self.weights)
+        self.n_spk = self.cfg.n_spk
+        self._ws = None
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h:
+            sf.sortformer_free(h)
+            self.handle = None
+
+    def workspace(self, nbytes: int) -> torch.Tensor:
+        if self._ws is None or self._ws.numel() < nbytes:
+            self._ws = _bytes(nbytes, self.device)
+        return self._ws
+
+    def offline(self, audio: torch.Tensor) -> torch.Tensor:
+        B, N = audio.shape
+        ws = self.workspace(sf.sortformer_offline_workspace_bytes(self.handle, B, N))
+        te = (N // 160 + 7) // 8
+        n_out = te if self.arch == "sortformer" else 8 * te
+        out = torch.empty(B, max(n_out, 1), self.n_spk, device=self.device)
+        got = sf.sortformer_forward_offline(self.handle, audio.contiguous(), out, ws)
+        return out[:, :got]
+
+    def encode_window(self, emb: torch.Tensor, n_valid: int | None = None):
+        B, W, _ = emb.shape
+        ws = self.workspace(sf.sortformer_encode_workspace_bytes(self.handle, B, W))
+        p = torch.empty(B, W, self.n_spk, device=self.device)
+        p10 = torch.empty(B, 8 * W, self.n_spk, device=self.device) \
+            if self.arch == "nemotron" else None
+        sf.sortformer_encode_window(self.handle, emb.contiguous(), W if n_valid is None else n_valid,
+                                    p, p10, ws)
+        return p if p10 is None else (p, p10)
+
+    def pre_encode(self, audio: torch.Tensor):
+        B, N = audio.shape
+        T = N // 160
+        te = (T + 7) // 8
+        ws = self.workspace(sf.sortformer_pre_encode_workspace_bytes(self.handle, B, N))
+        mel = torch.empty(B, max(T, 1), 128, device=self.device)
+        emb = torch.empty(B, max(te, 1), 512, device=self.device)
+        sf.sortformer_pre_encode(self.handle, audio.contiguous(), mel, emb, ws)
+        return mel[:, :T], emb[:, :te]
+
+    def stream(self, preset="low", batch: int = 1, config: sf.sf_stream_config | None = None):
+        return Stream(self, config if config is not None else sf.sortformer_stream_preset(preset),
+                      batch)
+
+
+class Stream:
+    def __init__(self, model: Model, scfg, batch: int = 1):
+        self.model, self.scfg, self.B = model, scfg, batch
+        nbytes = sf.sortformer_state_bytes(model.handle, scfg, batch)
+        if nbytes == 0:
+            raise ValueError("unsupported stream configuration")
+        self.state = _bytes(nbytes, model.device)
+        self.ws = _bytes(sf.sortformer_stream_workspace_bytes(model.handle, scfg, batch),
+                         model.device)
+        self.handle = sf.sortformer_stream_create(model.handle, scfg, batch, self.state)
+        self.out = torch.empty(batch, sf.sortformer_stream_max_emit(self.handle), model.n_spk,
+                               device=model.device)
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h:
+            sf.sortformer_stream_destroy(h)
+            self.handle = None
+
+    def samples_needed(self) -> int:
+        return sf.sortformer_stream_samples_needed(self.handle)
+
+    def step(self, audio_new: torch.Tensor, is_last: bool = False) -> torch.Tensor:
+        """audio_new (B, n) on the device -> this step's probabilities (B, n_emit, S)
+        (a view of a buffer the next step overwrites)."""
+        n = sf.sortformer_stream_step(self.handle, audio_new.contiguous(), audio_new.shape[1],
+                                      is_last, self.out, self.ws)
+        # the library writes the emitted rows densely as (B, n, S)
+        return self.out.view(-1)[:self.B * n * self.model.n_spk].view(self.B, n, self.model.n_spk)
+
+    def reset(self):
+        sf.sortformer_stream_reset(self.handle)
+
+    def info(self):
+        return sf.sortformer_stream_get_info(self.handle)
+
+    def run(self, audio: torch.Tensor) -> torch.Tensor:
+        """Feed a whole clip (B, N) the way a live stream would and return the
+        concatenated emitted probabilities."""
+        outs = []
+        pos, N = 0, audio.shape[1]
+        while True:
+            need = self.samples_needed()
+            if pos + need > N:  # the clip ends within this step's audio
+                outs.append(self.step(audio[:, pos:N], is_last=True).clone())
+                break
+            outs.append(self.step(audio[:, pos:pos + need]).clone())
+            pos += need
+        return torch.cat(outs, dim=1)

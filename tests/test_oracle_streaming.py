@@ -70,6 +70,29 @@ def test_pop_and_compression_cadence():
     assert len(log) == 60 and log[0][1] == 380 and max(W for _, W, *_ in log) == 756
 
 
+def test_live_schedule():
+    cfg = S.StreamConfig.preset("low")
+    sch = S.live_schedule(60 * 16000, cfg)
+    assert len(sch) == 124 and sch[-1] == (738, 12, 0, True)
+    assert all(s[1:] == (6, 7, False) for s in sch[:-1])
+    # samples needed accumulate to what each non-final step consumes
+    got = 0
+    for i, (c0, n, rc, last) in enumerate(sch[:-1]):
+        got += S.samples_needed(i, cfg)
+        assert got == 1280 * (c0 + n + rc) + 40
+    assert len(S.live_schedule(120 * 16000, S.StreamConfig.preset("ultra_low"))) == 500
+    vh = S.live_schedule(600 * 16000, S.StreamConfig.preset("very_high"))
+    assert len(vh) == 22 and vh[-1] == (7140, 360, 0, True)
+    # a clip shorter than the first window is one final step
+    assert S.live_schedule(1280 * 5, cfg) == [(0, 5, 0, True)]
+    # every frame is scored exactly once
+    for n in (1280 * 13 + 39, 1280 * 13 + 40, 1280 * 40 + 500, 160 * 7):
+        sch = S.live_schedule(n, cfg)
+        Te = (n // 160 + 7) // 8
+        cov = np.concatenate([np.arange(c0, c0 + k) for c0, k, _, _ in sch])
+        assert np.array_equal(cov, np.arange(Te))
+
+
 def test_fifo_conservation():
     cfg = S.StreamConfig(chunk_len=5, right_context=2, fifo_len=12, update_period=7,
                          spkcache_len=10_000)
