@@ -206,6 +206,15 @@ sf_status sortformer_stream_import(sf_stream* st, int32_t cache_len, int32_t fif
                                    const int32_t* flags, const double* sil_sum,
                                    const int32_t* sil_cnt, void* stream);
 
+/* Stream options. SF_STREAM_OPT_GRAPHS (default 1): each step's window
+ * forward (window copy + encoder + head) is captured once per distinct
+ * window shape into a HIP graph on an internal stream and replayed on the
+ * caller's stream; the frontend, pre_encode and the cache update stay
+ * direct launches. 0 launches every kernel directly. Results are identical
+ * either way. Graphs are rebuilt if the workspace pointer changes. */
+#define SF_STREAM_OPT_GRAPHS 1
+sf_status sortformer_stream_set_option(sf_stream* st, int32_t option, int32_t value);
+
 /* Test hook — the cache update alone (FIFO prediction refresh, chunk append,
  * pop with silence statistics, compression), given window probabilities
  * d_window_probs (B, W, S) with W = cache_len + fifo_len + lookahead_len of

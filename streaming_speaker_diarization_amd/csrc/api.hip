@@ -18,7 +18,10 @@ namespace {
 
 inline hipStream_t HS(void* s) { return static_cast<hipStream_t>(s); }
 inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
-inline sf_status launched() { return hipGetLastError() == hipSuccess ? SF_OK : SF_EHIP; }
+inline sf_status launched() {
+  if (take_gemm_failure()) return SF_ENOMEM;
+  return hipGetLastError() == hipSuccess ? SF_OK : SF_EHIP;
+}
 
 bool valid_stream_config(const sf_stream_config* c) {
   if (!c) return false;
@@ -40,7 +43,7 @@ long long ring_cap_for(const sf_stream_config* c) {
 
 // Byte layout of the state buffer.
 struct StateLayout {
-  size_t e, p, ph, sum, cnt, ring, total;
+  size_t e, p, ph, sum, cnt, slots, ring, total;
 };
 StateLayout state_layout(const sf_model* m, const sf_stream_config* c, int B) {
   const size_t cap = stream_cap(c), S = m->cfg.n_spk, D = 512;
@@ -50,8 +53,9 @@ StateLayout state_layout(const sf_model* m, const sf_stream_config* c, int B) {
   L.ph = al256((size_t)B * cap * 4);
   L.sum = al256((size_t)B * D * 8);
   L.cnt = al256((size_t)B * 4);
+  L.slots = al256((size_t)B * cap * 4);
   L.ring = al256((size_t)B * ring_cap_for(c) * 4);
-  L.total = 2 * (L.e + L.p + L.ph) + L.sum + L.cnt + L.ring;
+  L.total = 2 * (L.e + L.p + L.ph) + L.sum + L.cnt + L.slots + L.ring;
   return L;
 }
 
@@ -65,6 +69,7 @@ void bind_state(sf_stream* st, char* base) {
   }
   st->sil_sum = reinterpret_cast<double*>(p); p += L.sum;
   st->sil_cnt = reinterpret_cast<int*>(p); p += L.cnt;
+  st->slots = reinterpret_cast<int*>(p); p += L.slots;
   st->ring = reinterpret_cast<float*>(p);
 }
 
@@ -101,20 +106,62 @@ void state_update(sf_stream* st, const float* probs, int W, int n_chunk, hipStre
     const int k = std::max(0, per - st->sc.n_sil_per_spk);
     compress_cache(st->E[cur], st->P[cur], st->ph[cur], cap, D, S, B, st->Lc, st->Lf + st->Lp,
                    st->sil_sum, st->sil_cnt, C, per, k, st->E[cur ^ 1], st->P[cur ^ 1],
-                   st->ph[cur ^ 1], s);
+                   st->ph[cur ^ 1], st->slots, s);
     st->cur ^= 1;
     st->Lc = C;
   }
 }
 
+void drop_graphs(sf_stream* st) {
+  for (auto& kv : st->graphs) hipGraphExecDestroy(static_cast<hipGraphExec_t>(kv.second));
+  st->graphs.clear();
+}
+
+// Window copy + encoder for the current state, enqueued on s.
+void window_forward(sf_stream* st, EncWs& enc, hipStream_t s) {
+  const int W = st->Lc + st->Lf + st->Lp;
+  copy_rows(st->E[st->cur], (long long)st->cap * st->D, st->D, enc.x, (long long)W * st->D, st->D,
+            st->B, W, st->D, s);
+  encode(st->m, enc, st->B, W, W, s);
+}
+
+// Runs window_forward, through a cached graph when enabled. Returns false if
+// capture or instantiation failed (then the direct launch path was used).
+bool window_forward_graph(sf_stream* st, EncWs& enc, const void* ws, hipStream_t s) {
+  const int W = st->Lc + st->Lf + st->Lp;
+  const auto key = std::make_tuple(W, st->cur, ws);
+  auto it = st->graphs.find(key);
+  if (it == st->graphs.end()) {
+    if (!st->cap_stream) {
+      hipStream_t cs = nullptr;
+      if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) return false;
+      st->cap_stream = cs;
+    }
+    hipStream_t cs = static_cast<hipStream_t>(st->cap_stream);
+    hipGraph_t g = nullptr;
+    if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) return false;
+    window_forward(st, enc, cs);
+    if (hipStreamEndCapture(cs, &g) != hipSuccess || !g) return false;
+    hipGraphExec_t ex = nullptr;
+    const bool ok = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0) == hipSuccess;
+    hipGraphDestroy(g);
+    if (!ok) return false;
+    it = st->graphs.emplace(key, ex).first;
+  }
+  return hipGraphLaunch(static_cast<hipGraphExec_t>(it->second), s) == hipSuccess;
+}
+
 // One window forward on the current state, emitting the chunk rows.
 void step_core(sf_stream* st, int n_chunk, float* out, long long out_bstride, EncWs& enc,
-               hipStream_t s) {
+               const void* ws, hipStream_t s) {
   const sf_model* m = st->m;
   const int W = st->Lc + st->Lf + st->Lp, S = st->S, B = st->B;
-  copy_rows(st->E[st->cur], (long long)st->cap * st->D, st->D, enc.x, (long long)W * st->D, st->D,
-            B, W, st->D, s);
-  encode(m, enc, B, W, W, s);
+  bool done = false;
+  if (st->use_graphs && ws && !profiling()) done = window_forward_graph(st, enc, ws, s);
+  if (!done) {
+    (void)hipGetLastError();  // a failed capture must not leak its status
+    window_forward(st, enc, s);
+  }
   const int r0 = st->Lc + st->Lf;
   if (m->cfg.arch == SF_ARCH_SORTFORMER)
     copy_rows(enc.probs + (size_t)r0 * S, (long long)W * S, S, out, out_bstride, S, B, n_chunk, S, s);
@@ -284,6 +331,8 @@ sf_status sortformer_forward_offline(sf_model* m, const float* d_audio, int32_t 
   st.m = m;
   sortformer_stream_preset("nemotron_offline", &st.sc);
   st.B = B; st.S = S; st.D = 512;
+  st.use_graphs = false;
+  st.cap_stream = nullptr;
   st.cap = stream_cap(&st.sc);
   st.ring_cap = ring_cap_for(&st.sc);
   char* pre = p;
@@ -306,7 +355,7 @@ sf_status sortformer_forward_offline(sf_model* m, const float* d_audio, int32_t 
               e1 - st.enc_done, 512, s);
     st.Lp += e1 - st.enc_done;
     st.enc_done = e1;
-    step_core(&st, c1 - c0, d_probs + (size_t)8 * c0 * S, (long long)8 * Te * S, enc, s);
+    step_core(&st, c1 - c0, d_probs + (size_t)8 * c0 * S, (long long)8 * Te * S, enc, nullptr, s);
   }
   return launched();
 }
@@ -337,6 +386,8 @@ sf_status sortformer_stream_create(sf_model* m, const sf_stream_config* c, int32
   st->D = 512;
   st->cap = stream_cap(c);
   st->ring_cap = ring_cap_for(c);
+  st->use_graphs = true;
+  st->cap_stream = nullptr;
   bind_state(st, static_cast<char*>(d_state));
   reset_host(st);
   reset_device(st, HS(stream));
@@ -348,7 +399,22 @@ sf_status sortformer_stream_create(sf_model* m, const sf_stream_config* c, int32
   return SF_OK;
 }
 
-void sortformer_stream_destroy(sf_stream* st) { delete st; }
+void sortformer_stream_destroy(sf_stream* st) {
+  if (!st) return;
+  drop_graphs(st);
+  if (st->cap_stream) hipStreamDestroy(static_cast<hipStream_t>(st->cap_stream));
+  delete st;
+}
+
+sf_status sortformer_stream_set_option(sf_stream* st, int32_t option, int32_t value) {
+  if (!st) return SF_EINVAL;
+  if (option == SF_STREAM_OPT_GRAPHS) {
+    st->use_graphs = value != 0;
+    if (!st->use_graphs) drop_graphs(st);
+    return SF_OK;
+  }
+  return SF_EINVAL;
+}
 
 sf_status sortformer_stream_reset(sf_stream* st, void* stream) {
   if (!st) return SF_EINVAL;
@@ -398,7 +464,7 @@ sf_status sortformer_stream_step(sf_stream* st, const float* d_audio_new, int64_
   st->enc_done = e1;
   st->recv = N;
   if (n_chunk > 0)
-    step_core(st, n_chunk, d_probs_out, (long long)(*n_emitted) * st->S, enc, s);
+    step_core(st, n_chunk, d_probs_out, (long long)(*n_emitted) * st->S, enc, d_ws, s);
   st->steps += 1;
   st->emitted += n_chunk;
   st->finished = is_last != 0;

@@ -13,7 +13,8 @@
 // placeholders; trailing slots are placeholders. A placeholder carries the
 // running silence mean (float64 sum / count, rounded to fp32; zero before any
 // silence) and zero probabilities. The rows after the old cache (FIFO and
-// look-ahead) move up behind the new cache.
+// look-ahead) move up behind the new cache. Selection runs in one workgroup
+// per stream; the row copies are spread over one workgroup per row.
 // This file is built with floating-point contraction disabled.
 #include "kernels.h"
 
@@ -26,7 +27,7 @@ __global__ __launch_bounds__(512) void compress_kernel(const float* E, const flo
                                                        const int* ph, int cap, int D, int S,
                                                        int M, int tail, const double* sil_sum,
                                                        const int* sil_cnt, int C, int per, int k,
-                                                       float* E2, float* P2, int* ph2) {
+                                                       int* slots) {
   __shared__ double keys[CMP_MAXM * CMP_MAXS];   // -1 marks an ineligible (frame, speaker)
   __shared__ int slot_src[CMP_MAXM];
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -85,34 +86,43 @@ __global__ __launch_bounds__(512) void compress_kernel(const float* E, const flo
   for (int r = S * per + tid; r < C; r += blockDim.x) slot_src[r] = -1;
   __syncthreads();
 
-  float* E2b = E2 + (size_t)b * cap * D;
-  float* P2b = P2 + (size_t)b * cap * S;
-  int* ph2b = ph2 + (size_t)b * cap;
-  const int cnt = sil_cnt[b];
-  for (int i = tid; i < C * D; i += blockDim.x) {
-    const int r = i / D, d = i % D, src = slot_src[r];
-    float v;
-    if (src >= 0) v = Eb[(size_t)src * D + d];
-    else v = cnt > 0 ? (float)(sil_sum[(size_t)b * D + d] / (double)cnt) : 0.f;
-    E2b[(size_t)r * D + d] = v;
+  // slot map for the gather: >= 0 source frame, -1 placeholder
+  for (int r = tid; r < C; r += blockDim.x) slots[(size_t)b * cap + r] = slot_src[r];
+}
+
+// Builds the new cache (one workgroup per row): slot rows take their source
+// frame or the placeholder (silence mean, zero probabilities); the FIFO and
+// look-ahead rows that followed the old cache move up behind it.
+__global__ __launch_bounds__(128) void cache_gather_kernel(const float* E, const float* P,
+                                                           const int* ph, int cap, int D, int S,
+                                                           int M, int C, const int* slots,
+                                                           const double* sil_sum,
+                                                           const int* sil_cnt, float* E2, float* P2,
+                                                           int* ph2) {
+  const int r = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  const int src = r < C ? slots[(size_t)b * cap + r] : M + (r - C);
+  const float* Eb = E + (size_t)b * cap * D;
+  float* E2r = E2 + ((size_t)b * cap + r) * D;
+  if (src >= 0) {
+    for (int d = 4 * t; d < D; d += 512)
+      *reinterpret_cast<float4*>(E2r + d) = *reinterpret_cast<const float4*>(Eb + (size_t)src * D + d);
+  } else {
+    const int cnt = sil_cnt[b];
+    for (int d = t; d < D; d += 128)
+      E2r[d] = cnt > 0 ? (float)(sil_sum[(size_t)b * D + d] / (double)cnt) : 0.f;
   }
-  for (int i = tid; i < C * S; i += blockDim.x) {
-    const int r = i / S, src = slot_src[r];
-    P2b[i] = src >= 0 ? Pb[(size_t)src * S + i % S] : 0.f;
-  }
-  for (int r = tid; r < C; r += blockDim.x) ph2b[r] = slot_src[r] < 0;
-  for (int i = tid; i < tail * D; i += blockDim.x)
-    E2b[(size_t)C * D + i] = Eb[(size_t)M * D + i];
-  for (int i = tid; i < tail * S; i += blockDim.x) P2b[(size_t)C * S + i] = Pb[(size_t)M * S + i];
-  for (int r = tid; r < tail; r += blockDim.x) ph2b[C + r] = phb[M + r];
+  if (t < S) P2[((size_t)b * cap + r) * S + t] = src >= 0 ? P[((size_t)b * cap + src) * S + t] : 0.f;
+  if (t == 0) ph2[(size_t)b * cap + r] = src >= 0 ? (r < C ? 0 : ph[(size_t)b * cap + src]) : 1;
 }
 
 void compress_cache(const float* E, const float* P, const int* ph, int cap, int D, int S, int B,
                     int M, int tail, const double* sil_sum, const int* sil_cnt, int C, int per,
-                    int k, float* E2, float* P2, int* ph2, hipStream_t s) {
-  ProfScope ps(PROF_CACHE, s, 0.0, (double)B * ((double)M * (D + S + 1) * 4 + (double)(C + tail) * (D + S + 1) * 4));
+                    int k, float* E2, float* P2, int* ph2, int* slots, hipStream_t s) {
+  ProfScope ps(PROF_CACHE, s, 0.0, (double)B * ((double)M * (S + 1) * 4 + (double)(C + tail) * (D + S + 1) * 8));
   hipLaunchKernelGGL(compress_kernel, dim3(B), dim3(512), 0, s, E, P, ph, cap, D, S, M, tail,
-                     sil_sum, sil_cnt, C, per, k, E2, P2, ph2);
+                     sil_sum, sil_cnt, C, per, k, slots);
+  hipLaunchKernelGGL(cache_gather_kernel, dim3(C + tail, B), dim3(128), 0, s, E, P, ph, cap, D, S,
+                     M, C, slots, sil_sum, sil_cnt, E2, P2, ph2);
 }
 
 }  // namespace sf

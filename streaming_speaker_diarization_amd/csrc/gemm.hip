@@ -1,25 +1,171 @@
 // Dense GEMM for every Linear layer of the forward: C[M,N] = A[M,K] * W[N,K]^T
 // (PyTorch Linear layout, both operands K-contiguous) on MFMA, with the
 // elementwise work that follows each Linear fused into the epilogue (bias,
-// Swish, ReLU, GELU, GLU, scaled residual add).
+// Swish, ReLU, GELU, GLU) or, for residual branches, written as fp32
+// split-K partial sums that the following LayerNorm adds into the residual
+// stream (every residual Linear of the three encoders is followed by one).
 //
-// Tiling: 256 threads = 4 waves in a 2x2 grid; each wave owns a (BM/2)x(BN/2)
-// sub-tile made of 16x16 MFMA tiles. A and W tiles of BK columns are staged
-// through LDS (row stride padded by 16 bytes) with register double buffering:
-// the next K tile is fetched from global memory while the current one feeds
-// the matrix cores, and one barrier per K tile separates the two LDS buffers.
+// Two kernels, both 256 threads = 4 waves in a 2x2 grid of 16x16 MFMA tiles:
+//  * slice kernel (windows of up to a few thousand rows, the streaming case):
+//    a 64x64 output tile and one K-slice of at most 512 (bf16) / 256 (fp32)
+//    columns; the whole A and W slices are loaded into LDS with every global
+//    load in flight at once, so a launch pays the memory latency once instead
+//    of once per K tile. Longer K is split over blockIdx.z into fp32 partial
+//    sums, reduced in a fixed order (deterministic) by the consumer.
+//  * loop kernel (large batched windows): BMxBN tiles, BK-column K tiles
+//    double-buffered through registers and LDS.
 #include "kernels.h"
 
 namespace sf {
 
+template <int EPI, typename OutT>
+__device__ __forceinline__ void epi_store(const GemmArgs& g, int m, int n, float v) {
+  OutT* out = static_cast<OutT*>(g.out);
+  const size_t row = g.rpb ? (size_t)(m / g.rpb) * g.bstride + (size_t)(m % g.rpb) * g.ldo
+                           : (size_t)m * g.ldo;
+  if constexpr (EPI == EPI_SWISH) v = swishf_(v);
+  if constexpr (EPI == EPI_RELU) v = fmaxf(v, 0.f);
+  if constexpr (EPI == EPI_GELU) v = geluf_(v);
+  out[row + n] = from_f<OutT>(v);
+  if constexpr (EPI == EPI_STORE)
+    if (g.resid) g.resid[(size_t)m * g.ldr + n] = v;
+}
+
+// Q/K columns go to out, V columns to the per-head transposed buffer.
+template <typename OutT>
+__device__ __forceinline__ void qkv_store(const GemmArgs& g, int m, int n, float v) {
+  if (n < g.vcol) {
+    static_cast<OutT*>(g.out)[(size_t)m * g.ldo + n] = from_f<OutT>(v);
+  } else {
+    const int nn = n - g.vcol, hh = nn / g.vhd, d = nn % g.vhd;
+    const int bb = m / g.vrows, w = m % g.vrows, H = (g.N - g.vcol) / g.vhd;
+    static_cast<OutT*>(g.vt)[((size_t)(bb * H + hh) * g.vhd + d) * g.vpitch + w] = from_f<OutT>(v);
+  }
+}
+
+// Epilogue over one wave's TMxTN grid of 16x16 accumulators. Lane l holds
+// rows 4*(l/16)+r, column l%16 of each tile. GLU: the weight rows were
+// interleaved in blocks of 16 (value, gate), so tiles 2p and 2p+1 hold the
+// value and gate halves of the same 16 output columns.
+template <int EPI, typename OutT, int TM, int TN>
+__device__ __forceinline__ void epilogue(const GemmArgs& g, f32x4 (&acc)[TM][TN], int mb, int nb,
+                                         int lane, int split) {
+  if constexpr (EPI == EPI_GLU) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int p = 0; p < TN / 2; ++p) {
+        const int nn = nb + 32 * p;
+        const int na = nn + (lane & 15);
+        const float ba = g.bias ? g.bias[na] : 0.f, bg = g.bias ? g.bias[na + 16] : 0.f;
+        const int oc = nn / 2 + (lane & 15);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = mb + 16 * i + 4 * (lane >> 4) + r;
+          if (m < g.M) {
+            OutT* out = static_cast<OutT*>(g.out);
+            out[(size_t)m * g.ldo + oc] =
+                from_f<OutT>((acc[i][2 * p][r] + ba) * sigmoidf_(acc[i][2 * p + 1][r] + bg));
+          }
+        }
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int n = nb + 16 * j + (lane & 15);
+        const float bn = (EPI != EPI_PARTIAL && g.bias) ? g.bias[n] : 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = mb + 16 * i + 4 * (lane >> 4) + r;
+          if (m >= g.M) continue;
+          if constexpr (EPI == EPI_PARTIAL) {
+            float* part = static_cast<float*>(g.out);
+            part[((size_t)split * g.M + m) * g.N + n] = acc[i][j][r];
+          } else if constexpr (EPI == EPI_QKV) {
+            qkv_store<OutT>(g, m, n, acc[i][j][r] + bn);
+          } else {
+            epi_store<EPI, OutT>(g, m, n, acc[i][j][r] + bn);
+          }
+        }
+      }
+  }
+}
+
+// ------------------------------------------------------------ slice kernel
+template <typename T> struct SliceCfg;
+template <> struct SliceCfg<bf16_t> { static constexpr int KMAX = 512; };
+template <> struct SliceCfg<float> { static constexpr int KMAX = 256; };
+
+// KS (the slice width) is a template parameter so that every thread issues a
+// fixed number of unconditional 16-byte loads: rows past M read a clamped
+// (valid) row and are zeroed by a select afterwards, so no load sits behind a
+// branch and all of them are in flight together.
+template <typename T, typename OutT, int EPI, int KS>
+__global__ __launch_bounds__(256) void gemm_slice_kernel(GemmArgs g) {
+  constexpr int VEC = 16 / (int)sizeof(T);
+  constexpr int LD = KS + VEC;
+  constexpr int CPR = KS / VEC;
+  constexpr int NCH = 64 * CPR / 256;        // 16-byte chunks per thread per operand
+  static_assert(64 * CPR % 256 == 0, "slice width");
+  using M_ = MF<T>;
+  __shared__ __align__(16) T As[64 * LD];
+  __shared__ __align__(16) T Bs[64 * LD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int n0 = blockIdx.x * 64, m0 = blockIdx.y * 64, split = blockIdx.z;
+  const int k0 = split * KS;
+  const T* A = static_cast<const T*>(g.A);
+  const T* Wt = static_cast<const T*>(g.W);
+
+  vec16 ra[NCH], rb[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = tid + 256 * i, r = c / CPR, kc = (c % CPR) * VEC;
+    const int m = min(m0 + r, g.M - 1);
+    ra[i] = *reinterpret_cast<const vec16*>(A + (size_t)m * g.lda + k0 + kc);
+    rb[i] = *reinterpret_cast<const vec16*>(Wt + (size_t)(n0 + r) * g.ldw + k0 + kc);
+  }
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = tid + 256 * i, r = c / CPR, kc = (c % CPR) * VEC;
+    const bool live = m0 + r < g.M;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ra[i].w[q] = live ? ra[i].w[q] : 0u;
+    *reinterpret_cast<vec16*>(&As[r * LD + kc]) = ra[i];
+    *reinterpret_cast<vec16*>(&Bs[r * LD + kc]) = rb[i];
+  }
+  __syncthreads();
+
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const T* ap = &As[(wm * 32 + (lane & 15)) * LD];
+  const T* bp = &Bs[(wn * 32 + (lane & 15)) * LD];
+#pragma unroll 4
+  for (int k = 0; k < KS; k += M_::KI) {
+    typename M_::frag a0 = M_::ld(ap + k, lane), a1 = M_::ld(ap + 16 * LD + k, lane);
+    typename M_::frag b0 = M_::ld(bp + k, lane), b1 = M_::ld(bp + 16 * LD + k, lane);
+    acc[0][0] = M_::mma(a0, b0, acc[0][0]);
+    acc[0][1] = M_::mma(a0, b1, acc[0][1]);
+    acc[1][0] = M_::mma(a1, b0, acc[1][0]);
+    acc[1][1] = M_::mma(a1, b1, acc[1][1]);
+  }
+  epilogue<EPI, OutT, 2, 2>(g, acc, m0 + wm * 32, n0 + wn * 32, lane, split);
+}
+
+// ------------------------------------------------------------- loop kernel
 template <typename T, typename OutT, int BM, int BN, int EPI>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
+__global__ __launch_bounds__(256) void gemm_loop_kernel(GemmArgs g, int ks) {
   constexpr int VEC = 16 / (int)sizeof(T);
   constexpr int BK = sizeof(T) == 2 ? 64 : 32;
   constexpr int LDK = BK + VEC;
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int TM = WM / 16, TN = WN / 16;
-  constexpr int CPR = BK / VEC;              // 16-byte chunks per tile row
+  constexpr int CPR = BK / VEC;
   constexpr int A_IT = BM * CPR / 256;
   constexpr int B_IT = BN * CPR / 256;
   using M_ = MF<T>;
@@ -28,9 +174,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
-  const T* A = static_cast<const T*>(g.A);
-  const T* Wt = static_cast<const T*>(g.W);
+  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM, split = blockIdx.z;
+  const T* A = static_cast<const T*>(g.A) + (size_t)split * ks;
+  const T* Wt = static_cast<const T*>(g.W) + (size_t)split * ks;
 
   vec16 ra[A_IT], rb[B_IT];
   auto fetch = [&](int kt) {
@@ -38,9 +184,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < A_IT; ++i) {
       int c = tid + i * 256, r = c / CPR, kc = (c % CPR) * VEC;
-      int m = m0 + r;
-      if (m < g.M) ra[i] = *reinterpret_cast<const vec16*>(A + (size_t)m * g.lda + k0 + kc);
-      else ra[i] = vec16{{0u, 0u, 0u, 0u}};
+      const int m = min(m0 + r, g.M - 1);
+      ra[i] = *reinterpret_cast<const vec16*>(A + (size_t)m * g.lda + k0 + kc);
     }
 #pragma unroll
     for (int i = 0; i < B_IT; ++i) {
@@ -52,6 +197,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < A_IT; ++i) {
       int c = tid + i * 256, r = c / CPR, kc = (c % CPR) * VEC;
+      const bool live = m0 + r < g.M;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ra[i].w[q] = live ? ra[i].w[q] : 0u;
       *reinterpret_cast<vec16*>(&As[buf][r * LDK + kc]) = ra[i];
     }
 #pragma unroll
@@ -67,7 +215,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = g.K / BK;
+  const int nk = ks / BK;
   fetch(0);
   stash(0);
   __syncthreads();
@@ -91,106 +239,143 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     if (kt + 1 < nk) stash(cur ^ 1);
     __syncthreads();
   }
+  epilogue<EPI, OutT, TM, TN>(g, acc, m0 + wm * WM, n0 + wn * WN, lane, split);
+}
 
-  // ---------------------------------------------------------------- epilogue
-  OutT* out = static_cast<OutT*>(g.out);
-  auto orow = [&](int m) -> size_t {
-    return g.rpb ? (size_t)(m / g.rpb) * g.bstride + (size_t)(m % g.rpb) * g.ldo
-                 : (size_t)m * g.ldo;
-  };
-  if constexpr (EPI == EPI_GLU) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int p = 0; p < TN / 2; ++p) {
-        const int nb = n0 + wn * WN + 32 * p;      // multiple of 32
-        const int na = nb + (lane & 15);
-        const float ba = g.bias ? g.bias[na] : 0.f, bg = g.bias ? g.bias[na + 16] : 0.f;
-        const int oc = nb / 2 + (lane & 15);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = m0 + wm * WM + 16 * i + 4 * (lane >> 4) + r;
-          if (m < g.M) {
-            float a = acc[i][2 * p][r] + ba, gt = acc[i][2 * p + 1][r] + bg;
-            out[orow(m) + oc] = from_f<OutT>(a * sigmoidf_(gt));
-          }
+// ------------------------------------------------- split-K reduce + epilogue
+// v = sum_s part[s][m][n] (in split order) + bias[n], then the epilogue.
+template <typename OutT, int EPI>
+__global__ __launch_bounds__(256) void splitk_epi_kernel(GemmArgs g, const float* part, int ns) {
+  const int m = blockIdx.x;
+  const int ncol = EPI == EPI_GLU ? g.N / 2 : g.N;
+  for (int c = threadIdx.x; c < ncol; c += 256) {
+    auto red = [&](int n) {
+      float v = 0.f;
+      for (int s = 0; s < ns; ++s) v += part[((size_t)s * g.M + m) * g.N + n];
+      return v + (g.bias ? g.bias[n] : 0.f);
+    };
+    if constexpr (EPI == EPI_GLU) {
+      const int na = (c / 16) * 32 + (c % 16);
+      OutT* out = static_cast<OutT*>(g.out);
+      out[(size_t)m * g.ldo + c] = from_f<OutT>(red(na) * sigmoidf_(red(na + 16)));
+    } else if constexpr (EPI == EPI_QKV) {
+      qkv_store<OutT>(g, m, c, red(c));
+    } else {
+      epi_store<EPI, OutT>(g, m, c, red(c));
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dispatch
+// The K slicing depends only on K and the operand type (never on M), and
+// both kernels accumulate a slice in the same k order, so a row's result is
+// bit-identical whatever the window or batch size.
+template <typename T>
+static bool slice_ok(int ks) {
+  return sizeof(T) == 2 ? (ks == 512 || ks == 384 || ks == 256 || ks == 192 || ks == 128 || ks == 64)
+                        : (ks == 256 || ks == 192 || ks == 128 || ks == 64);
+}
+
+template <typename T>
+static int n_slices(int K) {
+  constexpr int KMAX = SliceCfg<T>::KMAX;
+  int ns = (K + KMAX - 1) / KMAX;
+  while (K % ns != 0 || !slice_ok<T>(K / ns)) ++ns;
+  return ns;
+}
+
+template <typename T, typename OutT, int EPI, int KS>
+static void slice_launch(const GemmArgs& g, int ns, hipStream_t s) {
+  dim3 grid(g.N / 64, (g.M + 63) / 64, ns);
+  hipLaunchKernelGGL((gemm_slice_kernel<T, OutT, EPI, KS>), grid, dim3(256), 0, s, g);
+}
+
+template <typename T, typename OutT, int EPI>
+static void launch_kernel(const GemmArgs& g, int ns, hipStream_t s) {
+  const int ks = g.K / ns;
+  if (g.M <= SLICE_MAX_ROWS) {
+    switch (ks) {
+      case 64: slice_launch<T, OutT, EPI, 64>(g, ns, s); break;
+      case 128: slice_launch<T, OutT, EPI, 128>(g, ns, s); break;
+      case 192: slice_launch<T, OutT, EPI, 192>(g, ns, s); break;
+      case 256: slice_launch<T, OutT, EPI, 256>(g, ns, s); break;
+      default:
+        if constexpr (sizeof(T) == 2) {
+          if (ks == 384) slice_launch<T, OutT, EPI, 384>(g, ns, s);
+          else slice_launch<T, OutT, EPI, 512>(g, ns, s);
         }
-      }
+    }
+  } else if (g.M > 1536 && g.N % 128 == 0) {
+    dim3 grid(g.N / 128, (g.M + 127) / 128, ns);
+    hipLaunchKernelGGL((gemm_loop_kernel<T, OutT, 128, 128, EPI>), grid, dim3(256), 0, s, g, ks);
   } else {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int n = n0 + wn * WN + 16 * j + (lane & 15);
-        const float bn = g.bias ? g.bias[n] : 0.f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = m0 + wm * WM + 16 * i + 4 * (lane >> 4) + r;
-          if (m >= g.M) continue;
-          float v = acc[i][j][r] + bn;
-          if constexpr (EPI == EPI_RESID) {
-            float* rp = g.resid + (size_t)m * g.ldr + n;
-            *rp = *rp + g.alpha * v;
-          } else {
-            if constexpr (EPI == EPI_SWISH) v = swishf_(v);
-            if constexpr (EPI == EPI_RELU) v = fmaxf(v, 0.f);
-            if constexpr (EPI == EPI_GELU) v = geluf_(v);
-            out[orow(m) + n] = from_f<OutT>(v);
-            if constexpr (EPI == EPI_STORE)
-              if (g.resid) g.resid[(size_t)m * g.ldr + n] = v;
-          }
-        }
-      }
+    dim3 grid(g.N / 64, (g.M + 63) / 64, ns);
+    hipLaunchKernelGGL((gemm_loop_kernel<T, OutT, 64, 64, EPI>), grid, dim3(256), 0, s, g, ks);
   }
 }
 
 template <typename T, typename OutT, int EPI>
-static void launch_tile(const GemmArgs& g, hipStream_t s) {
-  if (g.M > 1536 && g.N % 128 == 0) {
-    dim3 grid(g.N / 128, (g.M + 127) / 128);
-    hipLaunchKernelGGL((gemm_kernel<T, OutT, 128, 128, EPI>), grid, dim3(256), 0, s, g);
-  } else {
-    dim3 grid(g.N / 64, (g.M + 63) / 64);
-    hipLaunchKernelGGL((gemm_kernel<T, OutT, 64, 64, EPI>), grid, dim3(256), 0, s, g);
+static int launch(const GemmArgs& g, hipStream_t s) {
+  const int ns = n_slices<T>(g.K);
+  if (ns == 1 || EPI == EPI_PARTIAL) {
+    if (ns > 1 && ns > g.max_split) return -1;
+    launch_kernel<T, OutT, EPI>(g, ns, s);
+    return EPI == EPI_PARTIAL ? ns : 1;
   }
+  if (!g.part || ns > g.max_split) return -1;
+  GemmArgs p = g;
+  p.out = g.part;
+  launch_kernel<T, float, EPI_PARTIAL>(p, ns, s);
+  hipLaunchKernelGGL((splitk_epi_kernel<OutT, EPI>), dim3(g.M), dim3(256), 0, s, g,
+                     static_cast<const float*>(g.part), ns);
+  return 1;
 }
 
 template <typename T, typename OutT>
-static void launch_epi(const GemmArgs& g, int epi, hipStream_t s) {
+static int launch_epi(const GemmArgs& g, int epi, hipStream_t s) {
   switch (epi) {
-    case EPI_STORE: launch_tile<T, OutT, EPI_STORE>(g, s); break;
-    case EPI_SWISH: launch_tile<T, OutT, EPI_SWISH>(g, s); break;
-    case EPI_RELU: launch_tile<T, OutT, EPI_RELU>(g, s); break;
-    case EPI_GELU: launch_tile<T, OutT, EPI_GELU>(g, s); break;
-    default: break;
+    case EPI_STORE: return launch<T, OutT, EPI_STORE>(g, s);
+    case EPI_SWISH: return launch<T, OutT, EPI_SWISH>(g, s);
+    case EPI_RELU: return launch<T, OutT, EPI_RELU>(g, s);
+    case EPI_GELU: return launch<T, OutT, EPI_GELU>(g, s);
+    case EPI_QKV: return launch<T, OutT, EPI_QKV>(g, s);
+    default: return 0;
   }
 }
 
 // Shapes are validated by the caller: N % 64 == 0, K % 64 == 0, rows of A
-// and W 16-byte aligned.
-void gemm(const GemmArgs& g, int epi, bool bf16_in, bool bf16_out, hipStream_t s) {
-  if (g.M <= 0) return;
-  const double ie = bf16_in ? 2 : 4, oe = (epi == EPI_RESID) ? 8 : (bf16_out ? 2 : 4);
+// and W 16-byte aligned. Returns the number of partial slices written for
+// EPI_PARTIAL (1 otherwise), or -1 (nothing launched) when the partial-sum
+// scratch is missing or too small.
+static thread_local bool g_gemm_failed = false;
+
+bool take_gemm_failure() {
+  const bool f = g_gemm_failed;
+  g_gemm_failed = false;
+  return f;
+}
+
+void flag_launch_failure() { g_gemm_failed = true; }
+
+static int checked(int r) {
+  if (r < 0) g_gemm_failed = true;
+  return r;
+}
+
+int gemm(const GemmArgs& g, int epi, bool bf16_in, bool bf16_out, hipStream_t s) {
+  if (g.M <= 0) return 1;
+  const double ie = bf16_in ? 2 : 4, oe = (epi == EPI_PARTIAL) ? 4 : (bf16_out ? 2 : 4);
   const double on = epi == EPI_GLU ? 0.5 : 1.0;
   ProfScope ps(PROF_GEMM, s, 2.0 * g.M * g.N * g.K,
                ie * ((double)g.M * g.K + (double)g.N * g.K) + oe * on * g.M * g.N);
-  if (epi == EPI_RESID) {
-    if (bf16_in) launch_tile<bf16_t, float, EPI_RESID>(g, s);
-    else launch_tile<float, float, EPI_RESID>(g, s);
-    return;
-  }
-  if (epi == EPI_GLU) {
-    if (bf16_in) launch_tile<bf16_t, float, EPI_GLU>(g, s);
-    else launch_tile<float, float, EPI_GLU>(g, s);
-    return;
-  }
-  if (bf16_in) {
-    if (bf16_out) launch_epi<bf16_t, bf16_t>(g, epi, s);
-    else launch_epi<bf16_t, float>(g, epi, s);
-  } else {
-    if (bf16_out) launch_epi<float, bf16_t>(g, epi, s);
-    else launch_epi<float, float>(g, epi, s);
-  }
+  if (epi == EPI_PARTIAL)
+    return checked(bf16_in ? launch<bf16_t, float, EPI_PARTIAL>(g, s)
+                           : launch<float, float, EPI_PARTIAL>(g, s));
+  if (epi == EPI_GLU)
+    return checked(bf16_in ? launch<bf16_t, float, EPI_GLU>(g, s) : launch<float, float, EPI_GLU>(g, s));
+  if (bf16_in)
+    return checked(bf16_out ? launch_epi<bf16_t, bf16_t>(g, epi, s) : launch_epi<bf16_t, float>(g, epi, s));
+  return checked(bf16_out ? launch_epi<float, bf16_t>(g, epi, s) : launch_epi<float, float>(g, epi, s));
 }
 
 }  // namespace sf

@@ -2,7 +2,9 @@
 // arena of a model, and the streaming state.
 #pragma once
 #include <cstdint>
+#include <map>
 #include <string>
+#include <tuple>
 #include <vector>
 
 #include "sortformer.h"
@@ -58,6 +60,7 @@ struct sf_model {
   sfh::TfLayer tf[18];
   const float *h_w1t, *h_b1, *h_w2, *h_b2;
   float* pe;
+  float* init_part;  // split-K scratch used while deriving the position tables
   // Nemotron
   const void* in_w;
   const float* in_b;
@@ -79,9 +82,15 @@ struct sf_stream {
   int cur;
   double* sil_sum;
   int* sil_cnt;
+  int* slots;  // compression slot map (B, cap)
   float* ring;
   int Lc, Lf, Lp;
   long long steps, emitted, recv;
   int enc_done;
   bool finished;
+  // window-forward graphs keyed by (window rows, ping-pong buffer, workspace)
+  // (HIP handles kept opaque here: this header is also built by the host compiler)
+  bool use_graphs;
+  void* cap_stream;                                            // hipStream_t
+  std::map<std::tuple<int, int, const void*>, void*> graphs;   // hipGraphExec_t
 };

@@ -5,7 +5,14 @@
 
 namespace sf {
 
-enum { EPI_STORE = 0, EPI_SWISH = 1, EPI_RELU = 2, EPI_GELU = 3, EPI_RESID = 4, EPI_GLU = 5 };
+enum { EPI_STORE = 0, EPI_SWISH = 1, EPI_RELU = 2, EPI_GELU = 3, EPI_GLU = 5, EPI_PARTIAL = 6,
+       EPI_QKV = 7 };
+// Windows up to this many rows use the K-slice GEMM kernel.
+#define SLICE_MAX_ROWS 4096
+// fp32 partial-sum scratch per GEMM row: slices * N never exceeds this
+// (bf16: 4 x 512 residual branches; fp32: 8 x 512 or 2 x 2048; the 4096->512
+// subsampling output: 8 x 512 bf16, 16 x 512 fp32).
+#define PART_PER_ROW 8192
 
 struct GemmArgs {
   const void* A; int lda;   // (M, K) activations
@@ -15,15 +22,27 @@ struct GemmArgs {
   void* out; int ldo;       // (M, N) output (EPI_GLU: (M, N/2))
   int rpb;                  // rows per batch of the output (0: contiguous)
   long long bstride;        // output elements between batches when rpb != 0
-  float* resid; int ldr;    // EPI_RESID: resid += alpha*y; EPI_STORE: optional fp32 copy
-  float alpha;
+  float* resid; int ldr;    // EPI_STORE: optional fp32 copy of the output
+  void* part;               // fp32 scratch for split-K partial sums (may be null)
+  int max_split;            // most K slices the scratch (or, for EPI_PARTIAL, out) holds
+  // EPI_QKV: columns >= vcol (the V block) go to vt transposed per head,
+  // vt[((b*H + h)*hd + d)*vpitch + w] for row m = b*vrows + w.
+  void* vt; int vcol, vrows, vpitch, vhd;
 };
-void gemm(const GemmArgs& g, int epi, bool bf16_in, bool bf16_out, hipStream_t s);
+// EPI_PARTIAL writes fp32 partial sums (no bias) to out as [slice][M][N] and
+// returns the slice count; other epilogues return 1.
+int gemm(const GemmArgs& g, int epi, bool bf16_in, bool bf16_out, hipStream_t s);
+// True (and cleared) if a gemm() call since the last check launched nothing
+// because its partial-sum scratch was missing or too small.
+bool take_gemm_failure();
+// Records that a launcher refused its arguments (reported by take_gemm_failure).
+void flag_launch_failure();
 
 enum { ATT_PLAIN = 0, ATT_RELPOS = 1, ATT_ROPE = 2 };
 struct AttnArgs {
-  const void* qkv; int ldq;   // (B*W, ldq) rows, q/k/v column blocks
-  int qoff, koff, voff;
+  const void* qkv; int ldq;   // (B*W, ldq) rows, q/k column blocks
+  int qoff, koff;
+  const void* vt; int vpitch; // V transposed per head: (B, H, hd, vpitch), keys contiguous
   int B, H, W, n_valid;
   const float* ub; const float* vb;   // (H, hd) relative-position biases
   const void* P; int ldp; int p_center; // relative-position projections, row delta+p_center
@@ -33,8 +52,19 @@ struct AttnArgs {
 };
 void attention(const AttnArgs& a, int mode, int head_dim, bool bf16, hipStream_t s);
 
-void layernorm(const float* x, int M, int D, const float* g1, const float* b1, const float* g2,
-               const float* b2, float* y_f32, void* y_act, bool bf16, hipStream_t s);
+// LayerNorm over rows of the fp32 residual stream x (D = 512 or 192), with
+// the residual branch folded in: v = x + alpha*(sum_s part[s] + pbias) when
+// part is given (split-K partials of the branch's last Linear, [s][M][D]).
+// x_mode: 0 leave x, 1 x <- v, 2 x <- LN1(v). y_act <- LN2(LN1(v)) if g2
+// else LN1(v) (GEMM operand type), when non-null.
+struct LnArgs {
+  float* x; int M; int D;
+  const float* part; int nsplit; const float* pbias; float alpha;
+  const float *g1, *b1, *g2, *b2;
+  int x_mode;
+  void* y_act;
+};
+void layernorm(const LnArgs& a, bool bf16, hipStream_t s);
 
 void dwconv_time(const float* glu, int B, int W, int n_valid, const float* w9,
                  const float* scale, const float* shift, void* out, bool bf16, hipStream_t s);
@@ -69,7 +99,7 @@ void silence_update(const float* E, const float* P, int cap, int D, int S, int B
                     double* sil_sum, int* sil_cnt, hipStream_t s);
 void compress_cache(const float* E, const float* P, const int* ph, int cap, int D, int S, int B,
                     int M, int tail, const double* sil_sum, const int* sil_cnt, int C, int per,
-                    int k, float* E2, float* P2, int* ph2, hipStream_t s);
+                    int k, float* E2, float* P2, int* ph2, int* slots, hipStream_t s);
 
 // Benchmark profiling (see prof.hip). Classes match SF_PROF_* in the ABI.
 enum { PROF_GEMM = 1, PROF_ATTN = 2, PROF_LN = 3, PROF_CONV = 4, PROF_FRONTEND = 5, PROF_CACHE = 6 };
@@ -78,6 +108,7 @@ void prof_begin_launch(hipStream_t s);
 void prof_end_launch(hipStream_t s, double flops, double bytes);
 int prof_start(int cls, int max_launches);
 int prof_stop(double* ms, long long* launches, double* flops, double* bytes);
+bool profiling();  // any class being profiled (graph capture is then bypassed)
 
 // Brackets one launch with profiling events when its class is being profiled.
 struct ProfScope {

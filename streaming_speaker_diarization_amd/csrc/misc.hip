@@ -7,25 +7,43 @@
 namespace sf {
 
 // ------------------------------------------------------------- LayerNorm
-// One wave per row; statistics in fp32 (two passes over registers).
-// y = LN1(x); optionally z = LN2(y). y_f32 receives the last fp32 result that
-// feeds a residual stream (LN1 if LN2 exists, else LN1), y_act the operand of
-// the next GEMM (LN2 if present, else LN1).
-template <typename T, int D>
-__global__ __launch_bounds__(256) void ln_kernel(const float* x, int M, const float* g1,
-                                                 const float* b1, const float* g2, const float* b2,
-                                                 float* y_f32, T* y_act) {
+// One wave per row; statistics in fp32 (two passes over registers). The
+// residual partials are summed in slice order, so the result does not depend
+// on scheduling.
+template <typename T, int D, int NS>
+__global__ __launch_bounds__(256) void ln_kernel(LnArgs a) {
   constexpr int PER = D / 64;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (row >= M) return;
+  if (row >= a.M) return;
   float v[PER];
+  float* xr = a.x + (size_t)row * D;
+  // every load of the row (residual + NS partial slices) is issued before use
+  float pp[NS > 0 ? NS : 1][PER];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) v[i] = x[(size_t)row * D + lane + 64 * i];
+  for (int i = 0; i < PER; ++i) v[i] = xr[lane + 64 * i];
+#pragma unroll
+  for (int sp = 0; sp < NS; ++sp)
+#pragma unroll
+    for (int i = 0; i < PER; ++i) pp[sp][i] = a.part[((size_t)sp * a.M + row) * D + lane + 64 * i];
+  if constexpr (NS > 0) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = lane + 64 * i;
+      float t = 0.f;
+#pragma unroll
+      for (int sp = 0; sp < NS; ++sp) t += pp[sp][i];
+      v[i] += a.alpha * (t + a.pbias[c]);
+    }
+  }
+  if (a.x_mode == 1) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) xr[lane + 64 * i] = v[i];
+  }
   auto norm = [&](const float* gg, const float* bb) {
-    float s = 0.f;
+    float sm = 0.f;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) s += v[i];
-    const float mean = wave_sum(s) * (1.0f / D);
+    for (int i = 0; i < PER; ++i) sm += v[i];
+    const float mean = wave_sum(sm) * (1.0f / D);
     float q = 0.f;
 #pragma unroll
     for (int i = 0; i < PER; ++i) { v[i] -= mean; q += v[i] * v[i]; }
@@ -33,33 +51,50 @@ __global__ __launch_bounds__(256) void ln_kernel(const float* x, int M, const fl
 #pragma unroll
     for (int i = 0; i < PER; ++i) v[i] = v[i] * rstd * gg[lane + 64 * i] + bb[lane + 64 * i];
   };
-  norm(g1, b1);
-  if (y_f32) {
+  norm(a.g1, a.b1);
+  if (a.x_mode == 2) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) y_f32[(size_t)row * D + lane + 64 * i] = v[i];
+    for (int i = 0; i < PER; ++i) xr[lane + 64 * i] = v[i];
   }
-  if (g2) norm(g2, b2);
-  if (y_act) {
+  if (a.g2) norm(a.g2, a.b2);
+  if (a.y_act) {
+    T* y = static_cast<T*>(a.y_act) + (size_t)row * D;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) y_act[(size_t)row * D + lane + 64 * i] = from_f<T>(v[i]);
+    for (int i = 0; i < PER; ++i) y[lane + 64 * i] = from_f<T>(v[i]);
   }
 }
 
-void layernorm(const float* x, int M, int D, const float* g1, const float* b1, const float* g2,
-               const float* b2, float* y_f32, void* y_act, bool bf16, hipStream_t s) {
-  if (M <= 0) return;
-  ProfScope ps(PROF_LN, s, 0.0,
-               (double)M * D * (4.0 + (y_f32 ? 4.0 : 0.0) + (y_act ? (bf16 ? 2.0 : 4.0) : 0.0)));
-  dim3 grid((M + 3) / 4);
-#define LN_CASE(TT, DD)                                                                      \
-  hipLaunchKernelGGL((ln_kernel<TT, DD>), grid, dim3(256), 0, s, x, M, g1, b1, g2, b2, y_f32, \
-                     static_cast<TT*>(y_act))
-  if (bf16) {
-    if (D == 512) LN_CASE(bf16_t, 512); else LN_CASE(bf16_t, 192);
-  } else {
-    if (D == 512) LN_CASE(float, 512); else LN_CASE(float, 192);
+template <typename T, int D>
+static void ln_launch(const LnArgs& a, dim3 grid, hipStream_t s) {
+  switch (a.part ? a.nsplit : 0) {
+    case 0: hipLaunchKernelGGL((ln_kernel<T, D, 0>), grid, dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((ln_kernel<T, D, 1>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((ln_kernel<T, D, 2>), grid, dim3(256), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((ln_kernel<T, D, 3>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((ln_kernel<T, D, 4>), grid, dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((ln_kernel<T, D, 8>), grid, dim3(256), 0, s, a); break;
+    default: break;  // rejected by layernorm()
   }
-#undef LN_CASE
+}
+
+void layernorm(const LnArgs& a, bool bf16, hipStream_t s) {
+  if (a.M <= 0) return;
+  const int ns = a.part ? a.nsplit : 0;
+  if (ns < 0 || ns == 5 || ns == 6 || ns == 7 || ns > 8 || (ns > 0 && !a.pbias)) {
+    flag_launch_failure();
+    return;
+  }
+  ProfScope ps(PROF_LN, s, 0.0,
+               (double)a.M * a.D * (4.0 + 4.0 * ns + (a.x_mode ? 4.0 : 0.0) +
+                                    (a.y_act ? (bf16 ? 2.0 : 4.0) : 0.0)));
+  dim3 grid((a.M + 3) / 4);
+  if (bf16) {
+    if (a.D == 512) ln_launch<bf16_t, 512>(a, grid, s);
+    else ln_launch<bf16_t, 192>(a, grid, s);
+  } else {
+    if (a.D == 512) ln_launch<float, 512>(a, grid, s);
+    else ln_launch<float, 192>(a, grid, s);
+  }
 }
 
 // ------------------------------------------- conformer depthwise conv (k=9)
@@ -72,12 +107,20 @@ __global__ __launch_bounds__(256) void dwconv_time_kernel(const float* glu, int 
                                                           const float* sh, T* out) {
   const int t = blockIdx.x, b = blockIdx.y;
   const float* gb = glu + (size_t)b * W * 512;
-  for (int c = threadIdx.x; c < 512; c += 256) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = threadIdx.x + 256 * h;
+    float x[9];
+#pragma unroll
+    for (int k = 0; k < 9; ++k) {
+      const int tt = min(max(t + k - 4, 0), W - 1);
+      x[k] = gb[(size_t)tt * 512 + c];
+    }
     float acc = 0.f;
 #pragma unroll
     for (int k = 0; k < 9; ++k) {
       const int tt = t + k - 4;
-      if (tt >= 0 && tt < n_valid) acc += w9[c * 9 + k] * gb[(size_t)tt * 512 + c];
+      acc += (tt >= 0 && tt < n_valid) ? w9[c * 9 + k] * x[k] : 0.f;
     }
     out[((size_t)b * W + t) * 512 + c] = from_f<T>(swishf_(sc[c] * acc + sh[c]));
   }
@@ -117,12 +160,25 @@ __global__ __launch_bounds__(256) void logmel_kernel(const float* audio, long lo
   const int tid = threadIdx.x, b = blockIdx.y, f0 = blockIdx.x * 4;
   const float* ab = audio + (size_t)b * a_bstride;
   for (int i = tid; i < 512; i += 256) { tc[i] = tab[i]; ts[i] = tab[512 + i]; }
-  for (int i = tid; i < 4 * 400; i += 256) {
-    const int f = i / 400, n = i % 400;
-    const long long smp = 160 * (t0 + f0 + f) - 200 + n;
-    float v = 0.f;
-    if (f0 + f < nfr && smp >= 0 && smp < n_total) v = ab[smp & ring_mask] * tab[1024 + n];
-    xs[f][n] = v;
+  {
+    float v[7];
+#pragma unroll
+    for (int q = 0; q < 7; ++q) {  // 7 x 256 >= 4 x 400 samples
+      const int i = min(tid + 256 * q, 4 * 400 - 1), f = i / 400, n = i % 400;
+      const long long smp = 160 * (t0 + f0 + f) - 200 + n;
+      const long long sc = smp < 0 ? 0 : (smp >= n_total ? n_total - 1 : smp);
+      v[q] = ab[sc & ring_mask];
+    }
+#pragma unroll
+    for (int q = 0; q < 7; ++q) {
+      const int i = tid + 256 * q;
+      if (i < 4 * 400) {
+        const int f = i / 400, n = i % 400;
+        const long long smp = 160 * (t0 + f0 + f) - 200 + n;
+        const bool live = f0 + f < nfr && smp >= 0 && smp < n_total;
+        xs[f][n] = live ? v[q] * tab[1024 + n] : 0.f;
+      }
+    }
   }
   __syncthreads();
   for (int k = tid; k < 257; k += 256) {
@@ -169,18 +225,25 @@ __global__ __launch_bounds__(256) void conv0_kernel(const float* mel, long long 
                                                     const float* w, const float* bias) {
   const int o = blockIdx.x / 64, f = blockIdx.x % 64, b = blockIdx.y, c = threadIdx.x;
   const float* mb = mel + (size_t)b * mel_bstride;
-  float acc = bias[c];
+  const int r0 = 2 * (o_base + o) - 1;
+  const int rlo = max(r0, max(0, mel_base)), rhi = min(r0 + 2, T - 1);
+  float x[9];
 #pragma unroll
-  for (int a = 0; a < 3; ++a) {
-    const int r = 2 * (o_base + o) - 1 + a;
-    if (r < 0 || r >= T) continue;
+  for (int a = 0; a < 3; ++a)
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
-      const int col = 2 * f - 1 + q;
-      if (col < 0 || col >= 128) continue;
-      acc += w[c * 9 + a * 3 + q] * mb[(size_t)(r - mel_base) * 128 + col];
+      const int r = min(max(r0 + a, rlo), rhi), col = min(max(2 * f - 1 + q, 0), 127);
+      x[a * 3 + q] = mb[(size_t)(r - mel_base) * 128 + col];
     }
-  }
+  float acc = bias[c];
+#pragma unroll
+  for (int a = 0; a < 3; ++a)
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const int r = r0 + a, col = 2 * f - 1 + q;
+      const bool live = r >= 0 && r < T && col >= 0 && col < 128;
+      acc += live ? w[c * 9 + a * 3 + q] * x[a * 3 + q] : 0.f;
+    }
   out[(size_t)b * out_bstride + ((size_t)o * 64 + f) * 256 + c] = fmaxf(acc, 0.f);
 }
 
@@ -200,18 +263,25 @@ __global__ __launch_bounds__(256) void dw2d_kernel(const float* in, long long in
   const int f_out = (f_in + 1) / 2;
   const int o = blockIdx.x / f_out, f = blockIdx.x % f_out, b = blockIdx.y, c = threadIdx.x;
   const float* ib = in + (size_t)b * in_bstride;
-  float acc = bias[c];
+  const int r0 = 2 * (o_base + o) - 1;
+  const int rlo = max(r0, max(0, in_base)), rhi = min(r0 + 2, len_in - 1);
+  float x[9];
 #pragma unroll
-  for (int a = 0; a < 3; ++a) {
-    const int r = 2 * (o_base + o) - 1 + a;
-    if (r < 0 || r >= len_in) continue;
+  for (int a = 0; a < 3; ++a)
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
-      const int col = 2 * f - 1 + q;
-      if (col < 0 || col >= f_in) continue;
-      acc += w[c * 9 + a * 3 + q] * ib[((size_t)(r - in_base) * f_in + col) * 256 + c];
+      const int r = min(max(r0 + a, rlo), rhi), col = min(max(2 * f - 1 + q, 0), f_in - 1);
+      x[a * 3 + q] = ib[((size_t)(r - in_base) * f_in + col) * 256 + c];
     }
-  }
+  float acc = bias[c];
+#pragma unroll
+  for (int a = 0; a < 3; ++a)
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const int r = r0 + a, col = 2 * f - 1 + q;
+      const bool live = r >= 0 && r < len_in && col >= 0 && col < f_in;
+      acc += live ? w[c * 9 + a * 3 + q] * x[a * 3 + q] : 0.f;
+    }
   out[(size_t)b * out_bstride + ((size_t)o * f_out + f) * 256 + c] = from_f<T>(acc);
 }
 
@@ -233,10 +303,17 @@ template <typename OT>
 __global__ __launch_bounds__(256) void stack8_kernel(const float* mel, long long mel_bstride,
                                                      int mel_base, int T, int e0, int n, OT* out) {
   const int j = blockIdx.x, b = blockIdx.y;
-  for (int i = threadIdx.x; i < 1024; i += 256) {
-    const int r = i >> 7, m = i & 127, t = 8 * (e0 + j) + r;
-    const float v = t < T ? mel[(size_t)b * mel_bstride + (size_t)(t - mel_base) * 128 + m] : 0.f;
-    out[((size_t)b * n + j) * 1024 + i] = from_f<OT>(v);
+  float v[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = threadIdx.x + 256 * q, r = i >> 7, m = i & 127;
+    const int t = min(8 * (e0 + j) + r, T - 1);
+    v[q] = mel[(size_t)b * mel_bstride + (size_t)(t - mel_base) * 128 + m];
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = threadIdx.x + 256 * q, r = i >> 7;
+    out[((size_t)b * n + j) * 1024 + i] = from_f<OT>(8 * (e0 + j) + r < T ? v[q] : 0.f);
   }
 }
 
@@ -258,7 +335,11 @@ __global__ __launch_bounds__(192) void head_sf_kernel(const float* x, int M, con
                                                       const float* b2, int S, float* probs) {
   __shared__ float xs[8][192], hs[8][192];
   const int r0 = blockIdx.x * 8, t = threadIdx.x;
-  for (int r = 0; r < 8; ++r) xs[r][t] = r0 + r < M ? x[(size_t)(r0 + r) * 192 + t] : 0.f;
+  float xv[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) xv[r] = x[(size_t)min(r0 + r, M - 1) * 192 + t];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) xs[r][t] = r0 + r < M ? xv[r] : 0.f;
   __syncthreads();
   float acc[8];
 #pragma unroll
@@ -390,22 +471,35 @@ void refresh_probs(const float* wp, int W, int S, int B, int Lc, int nrows, floa
 // order; a frame whose largest probability is <= 0.5 adds its embedding to
 // the float64 running sum (one thread per dimension, so the additions happen
 // in frame order) and increments the count.
-__global__ void silence_kernel(const float* E, const float* P, int cap, int D, int S, int r0,
-                               int n, double* sum, int* cnt) {
+__global__ __launch_bounds__(512) void silence_kernel(const float* E, const float* P, int cap, int D,
+                                                      int S, int r0, int n, double* sum, int* cnt) {
+  __shared__ unsigned char silent[1024];
   const int b = blockIdx.x;
   const float* Eb = E + (size_t)b * cap * D;
   const float* Pb = P + (size_t)b * cap * S;
+  for (int r = threadIdx.x; r < n; r += blockDim.x) {
+    float mx = Pb[(size_t)(r0 + r) * S];
+    for (int sp = 1; sp < S; ++sp) mx = fmaxf(mx, Pb[(size_t)(r0 + r) * S + sp]);
+    silent[r] = mx <= 0.5f;
+  }
+  __syncthreads();
   int added = 0;
+  for (int r = 0; r < n; ++r) added += silent[r];
   for (int d = threadIdx.x; d < D; d += blockDim.x) {
     double acc = sum[(size_t)b * D + d];
-    int a = 0;
-    for (int r = r0; r < r0 + n; ++r) {
-      float mx = Pb[(size_t)r * S];
-      for (int sp = 1; sp < S; ++sp) mx = fmaxf(mx, Pb[(size_t)r * S + sp]);
-      if (mx <= 0.5f) { acc += (double)Eb[(size_t)r * D + d]; ++a; }
+    int r = 0;
+    for (; r + 8 <= n; r += 8) {  // eight loads in flight, added in frame order
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = Eb[(size_t)(r0 + r + q) * D + d];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc = silent[r + q] ? acc + (double)v[q] : acc;
+    }
+    for (; r < n; ++r) {
+      const float v = Eb[(size_t)(r0 + r) * D + d];
+      acc = silent[r] ? acc + (double)v : acc;
     }
     sum[(size_t)b * D + d] = acc;
-    added = a;
   }
   if (threadIdx.x == 0) cnt[b] += added;
 }

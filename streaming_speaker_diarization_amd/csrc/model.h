@@ -14,6 +14,10 @@ struct EncWs {
   float* glu;     // (B*W, 512) GLU output
   float* probs;   // (B*W, S) 80 ms probabilities
   float* probs10; // (B*8W, S) 10 ms probabilities (Nemotron)
+  float* part;    // split-K partial sums of residual-branch Linears
+  size_t part_floats;
+  void* vt;       // (B, H, head dim, vpitch) V transposed per head
+  int vpitch;     // keys per V^T row (window rounded up to 8)
 };
 
 bool valid_config(const sf_model_config* c);

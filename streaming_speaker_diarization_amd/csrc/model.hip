@@ -169,6 +169,8 @@ void build_sortformer(sf_model* m, Arena& A, const Src& s) {
       L.wpos = const_cast<float*>(A.f32(have ? w.data() : nullptr, 512 * 512));
     }
     L.P = A.raw((size_t)(2 * SF_MAX_WINDOW - 1) * 512 * m->esz);
+    if (l == 0)  // split-K scratch of the projection GEMMs at init
+      m->init_part = static_cast<float*>(A.raw((size_t)(2 * SF_MAX_WINDOW - 1) * 4 * 512 * 4));
     L.conv_g = A.f32(s.get(p + "conv.ln.g"), 512);
     L.conv_b = A.f32(s.get(p + "conv.ln.b"), 512);
     {  // pointwise-1 rows interleaved in blocks of 16 (value, gate) for the GLU epilogue
@@ -383,15 +385,21 @@ sf_status init_model(sf_model* m, void* d_weights, size_t bytes, hipStream_t st)
       g.bias = nullptr;
       g.M = 2 * SF_MAX_WINDOW - 1; g.N = 512; g.K = 512;
       g.out = m->conf[l].P; g.ldo = 512;
+      g.part = m->init_part; g.max_split = 4;
       gemm(g, EPI_STORE, false, m->bf16, st);
     }
   }
+  if (take_gemm_failure()) return SF_ENOMEM;
   if (hipStreamSynchronize(st) != hipSuccess) return SF_EHIP;
   if (hipGetLastError() != hipSuccess) return SF_EHIP;
   return SF_OK;
 }
 
 // ---------------------------------------------------------- workspaces
+// fp32 scratch for split-K partial sums of the encoder: room for
+// [slices][rows][N] with slices * N <= 4096.
+size_t part_floats(size_t rows) { return rows * 4096; }
+
 size_t enc_ws_bytes(const sf_model* m, int B, int W) {
   const size_t r = (size_t)B * W, es = m->esz;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -403,6 +411,8 @@ size_t enc_ws_bytes(const sf_model* m, int B, int W) {
   t += al(r * 512 * 4);   // glu
   t += al(r * 8 * 4);     // probs
   t += al(r * 64 * 4);    // probs10
+  t += al(part_floats(r) * 4);
+  t += al((size_t)B * 512 * (W + 8) * es);  // V transposed per head
   return t;
 }
 
@@ -421,6 +431,10 @@ EncWs carve_enc(const sf_model* m, char* p, int B, int W) {
   w.glu = reinterpret_cast<float*>(take(r * 512 * 4));
   w.probs = reinterpret_cast<float*>(take(r * 8 * 4));
   w.probs10 = reinterpret_cast<float*>(take(r * 64 * 4));
+  w.part_floats = part_floats(r);
+  w.part = reinterpret_cast<float*>(take(w.part_floats * 4));
+  w.vpitch = (W + 7) / 8 * 8;
+  w.vt = take((size_t)B * 512 * (W + 8) * es);
   return w;
 }
 
@@ -437,6 +451,7 @@ size_t pre_ws_bytes(const sf_model* m, int B, int n) {
   } else {
     t += al(b * nn * 1024 * es);           // stacked frames
   }
+  t += al(b * nn * PART_PER_ROW * 4);  // split-K partials
   return t;
 }
 
@@ -461,6 +476,8 @@ void pre_encode_range(const sf_model* m, const float* audio, long long a_bstride
     const int t0 = std::max(0, 8 * e0 - 8), t1 = std::min(T, 8 * e1);
     const int a1 = std::max(0, 4 * e0 - 3), b1 = std::min(T1, 4 * e1);
     const int a2 = std::max(0, 2 * e0 - 1), b2 = std::min(T2, 2 * e1);
+    float* part = reinterpret_cast<float*>(p);
+    p += al((size_t)B * nn * PART_PER_ROW * 4);
     float* l1 = reinterpret_cast<float*>(p);
     p += al((size_t)B * 4 * nn * 64 * 256 * 4);
     void* d1 = p;
@@ -489,9 +506,12 @@ void pre_encode_range(const sf_model* m, const float* audio, long long a_bstride
     g = GemmArgs{};
     g.A = p2; g.lda = 4096; g.W = m->pre_out_w; g.ldw = 4096; g.bias = m->pre_out_b;
     g.M = B * n; g.N = 512; g.K = 4096; g.out = dst; g.ldo = 512; g.rpb = n; g.bstride = dst_bstride;
+    g.part = part; g.max_split = PART_PER_ROW / 512;
     gemm(g, EPI_STORE, bf, false, s);
   } else {
     const int t0 = 8 * e0, t1 = std::min(T, 8 * e1);
+    float* part = reinterpret_cast<float*>(p);
+    p += al((size_t)B * nn * PART_PER_ROW * 4);
     void* st = p;
     const long long mel_bs = (long long)std::max(0, t1 - t0) * 128;
     logmel(audio, a_bstride, ring_mask, n_total, t0, t1 - t0, B, m->fe_tab, mel, mel_bs, s);
@@ -499,108 +519,136 @@ void pre_encode_range(const sf_model* m, const float* audio, long long a_bstride
     GemmArgs g{};
     g.A = st; g.lda = 1024; g.W = m->in_w; g.ldw = 1024; g.bias = m->in_b;
     g.M = B * n; g.N = 512; g.K = 1024; g.out = dst; g.ldo = 512; g.rpb = n; g.bstride = dst_bstride;
+    g.part = part; g.max_split = PART_PER_ROW / 512;
     gemm(g, EPI_STORE, bf, false, s);
   }
 }
 
 // ------------------------------------------------------------- encoders
-static void gemm_(const void* A, int lda, const void* W, int ldw, const float* bias, int M, int N,
-                  int K, void* out, int ldo, int epi, bool bf_in, bool bf_out, hipStream_t s,
-                  float* resid = nullptr, int ldr = 0, float alpha = 1.f) {
-  GemmArgs g{};
-  g.A = A; g.lda = lda; g.W = W; g.ldw = ldw; g.bias = bias; g.M = M; g.N = N; g.K = K;
-  g.out = out; g.ldo = ldo; g.resid = resid; g.ldr = ldr; g.alpha = alpha;
-  gemm(g, epi, bf_in, bf_out, s);
-}
+namespace {
+struct Ctx {
+  const sf_model* m;
+  EncWs& w;
+  int M;
+  hipStream_t s;
+  bool bf;
+  // Linear with a fused epilogue into `out`.
+  void lin(const void* A, int lda, const void* W, const float* bias, int N, int K, void* out,
+           int ldo, int epi, bool bf_out, float* resid = nullptr, int ldr = 0) {
+    GemmArgs g{};
+    g.A = A; g.lda = lda; g.W = W; g.ldw = K; g.bias = bias; g.M = M; g.N = N; g.K = K;
+    g.out = out; g.ldo = ldo; g.resid = resid; g.ldr = ldr;
+    g.part = w.part; g.max_split = (int)(w.part_floats / ((size_t)M * N));
+    gemm(g, epi, bf, bf_out, s);
+  }
+  // Fused Q/K/V projection: Q and K into `out`, V transposed per head into w.vt.
+  void qkv(const void* A, int d, const void* W, const float* bias, void* out, int hd, int rows) {
+    GemmArgs g{};
+    g.A = A; g.lda = d; g.W = W; g.ldw = d; g.bias = bias; g.M = M; g.N = 3 * d; g.K = d;
+    g.out = out; g.ldo = 3 * d;
+    g.part = w.part; g.max_split = (int)(w.part_floats / ((size_t)M * 3 * d));
+    g.vt = w.vt; g.vcol = 2 * d; g.vrows = rows; g.vpitch = w.vpitch; g.vhd = hd;
+    gemm(g, EPI_QKV, bf, bf, s);
+  }
+  // Residual-branch Linear: fp32 partial sums for the next LayerNorm.
+  int branch(const void* A, int lda, const void* W, int N, int K) {
+    GemmArgs g{};
+    g.A = A; g.lda = lda; g.W = W; g.ldw = K; g.M = M; g.N = N; g.K = K;
+    g.out = w.part; g.ldo = N; g.max_split = (int)(w.part_floats / ((size_t)M * N));
+    return gemm(g, EPI_PARTIAL, bf, false, s);
+  }
+  // LayerNorm(s) with the pending residual branch (ns partial slices) folded in.
+  void ln(int D, int ns, const float* pbias, float alpha, const float* g1, const float* b1,
+          const float* g2, const float* b2, int x_mode, void* y_act) {
+    LnArgs a{};
+    a.x = w.x; a.M = M; a.D = D;
+    a.part = ns > 0 ? w.part : nullptr; a.nsplit = ns; a.pbias = pbias; a.alpha = alpha;
+    a.g1 = g1; a.b1 = b1; a.g2 = g2; a.b2 = b2; a.x_mode = x_mode; a.y_act = y_act;
+    layernorm(a, bf, s);
+  }
+};
+}  // namespace
 
 static void encode_sortformer(const sf_model* m, EncWs& w, int B, int W, int n_valid,
                               hipStream_t s) {
   const bool bf = m->bf16;
-  const int M = B * W;
-  float* x = w.x;
-  layernorm(x, M, 512, m->conf[0].ff1_g, m->conf[0].ff1_b, nullptr, nullptr, nullptr, w.h, bf, s);
+  Ctx c{m, w, B * W, s, bf};
+  c.ln(512, 0, nullptr, 0.f, m->conf[0].ff1_g, m->conf[0].ff1_b, nullptr, nullptr, 0, w.h);
   for (int l = 0; l < 17; ++l) {
     const ConfLayer& L = m->conf[l];
-    // macaron FFN, first half
-    gemm_(w.h, 512, L.ff1_w1, 512, L.ff1_b1, M, 2048, 512, w.big, 2048, EPI_SWISH, bf, bf, s);
-    gemm_(w.big, 2048, L.ff1_w2, 2048, L.ff1_b2, M, 512, 2048, nullptr, 0, EPI_RESID, bf, false, s,
-          x, 512, 0.5f);
+    // macaron FFN, first half: x += FF(LN(x))/2
+    c.lin(w.h, 512, L.ff1_w1, L.ff1_b1, 2048, 512, w.big, 2048, EPI_SWISH, bf);
+    int ns = c.branch(w.big, 2048, L.ff1_w2, 512, 2048);
+    c.ln(512, ns, L.ff1_b2, 0.5f, L.att_g, L.att_b, nullptr, nullptr, 1, w.h);
     // relative-position self-attention
-    layernorm(x, M, 512, L.att_g, L.att_b, nullptr, nullptr, nullptr, w.h, bf, s);
-    gemm_(w.h, 512, L.wqkv, 512, L.bqkv, M, 1536, 512, w.big, 1536, EPI_STORE, bf, bf, s);
+    c.qkv(w.h, 512, L.wqkv, L.bqkv, w.big, 64, W);
     AttnArgs a{};
-    a.qkv = w.big; a.ldq = 1536; a.qoff = 0; a.koff = 512; a.voff = 1024;
+    a.qkv = w.big; a.ldq = 1536; a.qoff = 0; a.koff = 512; a.vt = w.vt; a.vpitch = w.vpitch;
     a.B = B; a.H = 8; a.W = W; a.n_valid = n_valid;
     a.ub = L.u; a.vb = L.v; a.P = L.P; a.ldp = 512; a.p_center = SF_MAX_WINDOW - 1;
     a.ctx = w.ctx; a.ldc = 512; a.scale = 0.125f;
     attention(a, ATT_RELPOS, 64, bf, s);
-    gemm_(w.ctx, 512, L.wo, 512, L.bo, M, 512, 512, nullptr, 0, EPI_RESID, bf, false, s, x, 512,
-          1.f);
+    ns = c.branch(w.ctx, 512, L.wo, 512, 512);
+    c.ln(512, ns, L.bo, 1.f, L.conv_g, L.conv_b, nullptr, nullptr, 1, w.h);
     // convolution module
-    layernorm(x, M, 512, L.conv_g, L.conv_b, nullptr, nullptr, nullptr, w.h, bf, s);
-    gemm_(w.h, 512, L.pw1, 512, L.pw1_b, M, 1024, 512, w.glu, 512, EPI_GLU, bf, false, s);
+    c.lin(w.h, 512, L.pw1, L.pw1_b, 1024, 512, w.glu, 512, EPI_GLU, false);
     dwconv_time(w.glu, B, W, n_valid, L.dw9, L.dw_sc, L.dw_sh, w.h, bf, s);
-    gemm_(w.h, 512, L.pw2, 512, L.pw2_b, M, 512, 512, nullptr, 0, EPI_RESID, bf, false, s, x, 512,
-          1.f);
-    // macaron FFN, second half
-    layernorm(x, M, 512, L.ff2_g, L.ff2_b, nullptr, nullptr, nullptr, w.h, bf, s);
-    gemm_(w.h, 512, L.ff2_w1, 512, L.ff2_b1, M, 2048, 512, w.big, 2048, EPI_SWISH, bf, bf, s);
-    gemm_(w.big, 2048, L.ff2_w2, 2048, L.ff2_b2, M, 512, 2048, nullptr, 0, EPI_RESID, bf, false, s,
-          x, 512, 0.5f);
-    // output LayerNorm (fused with the next layer's first LayerNorm)
+    ns = c.branch(w.h, 512, L.pw2, 512, 512);
+    c.ln(512, ns, L.pw2_b, 1.f, L.ff2_g, L.ff2_b, nullptr, nullptr, 1, w.h);
+    // macaron FFN, second half, then the output LayerNorm (fused with the
+    // next layer's first LayerNorm)
+    c.lin(w.h, 512, L.ff2_w1, L.ff2_b1, 2048, 512, w.big, 2048, EPI_SWISH, bf);
+    ns = c.branch(w.big, 2048, L.ff2_w2, 512, 2048);
     if (l < 16)
-      layernorm(x, M, 512, L.out_g, L.out_b, m->conf[l + 1].ff1_g, m->conf[l + 1].ff1_b, x, w.h,
-                bf, s);
+      c.ln(512, ns, L.ff2_b2, 0.5f, L.out_g, L.out_b, m->conf[l + 1].ff1_g, m->conf[l + 1].ff1_b,
+           2, w.h);
     else
-      layernorm(x, M, 512, L.out_g, L.out_b, nullptr, nullptr, nullptr, w.h, bf, s);
+      c.ln(512, ns, L.ff2_b2, 0.5f, L.out_g, L.out_b, nullptr, nullptr, 0, w.h);
   }
-  // encoder_proj: fp32 residual stream for the transformer + GEMM operand
-  gemm_(w.h, 512, m->proj_w, 512, m->proj_b, M, 192, 512, w.ctx, 192, EPI_STORE, bf, bf, s, x,
-        192);
+  // encoder_proj: fp32 residual stream of the transformer + GEMM operand
+  c.lin(w.h, 512, m->proj_w, m->proj_b, 192, 512, w.ctx, 192, EPI_STORE, bf, w.x, 192);
   const void* hin = w.ctx;
   for (int l = 0; l < 18; ++l) {
     const TfLayer& L = m->tf[l];
-    gemm_(hin, 192, L.wqkv, 192, L.bqkv, M, 576, 192, w.big, 576, EPI_STORE, bf, bf, s);
+    c.qkv(hin, 192, L.wqkv, L.bqkv, w.big, 24, W);
     AttnArgs a{};
-    a.qkv = w.big; a.ldq = 576; a.qoff = 0; a.koff = 192; a.voff = 384;
+    a.qkv = w.big; a.ldq = 576; a.qoff = 0; a.koff = 192; a.vt = w.vt; a.vpitch = w.vpitch;
     a.B = B; a.H = 8; a.W = W; a.n_valid = n_valid;
     a.ctx = w.ctx; a.ldc = 192; a.scale = 1.0f / std::sqrt(24.0f);
     attention(a, ATT_PLAIN, 24, bf, s);
-    gemm_(w.ctx, 192, L.wo, 192, L.bo, M, 192, 192, nullptr, 0, EPI_RESID, bf, false, s, x, 192,
-          1.f);
-    layernorm(x, M, 192, L.ln1_g, L.ln1_b, nullptr, nullptr, x, w.h, bf, s);
-    gemm_(w.h, 192, L.w1, 192, L.b1, M, 768, 192, w.big, 768, EPI_RELU, bf, bf, s);
-    gemm_(w.big, 768, L.w2, 768, L.b2, M, 192, 768, nullptr, 0, EPI_RESID, bf, false, s, x, 192,
-          1.f);
-    layernorm(x, M, 192, L.ln2_g, L.ln2_b, nullptr, nullptr, x, w.h, bf, s);
+    int ns = c.branch(w.ctx, 192, L.wo, 192, 192);
+    c.ln(192, ns, L.bo, 1.f, L.ln1_g, L.ln1_b, nullptr, nullptr, 2, w.h);   // post-LN
+    c.lin(w.h, 192, L.w1, L.b1, 768, 192, w.big, 768, EPI_RELU, bf);
+    ns = c.branch(w.big, 768, L.w2, 192, 768);
+    c.ln(192, ns, L.b2, 1.f, L.ln2_g, L.ln2_b, nullptr, nullptr, 2, w.h);
     hin = w.h;
   }
-  head_sortformer(x, M, m->h_w1t, m->h_b1, m->h_w2, m->h_b2, m->cfg.n_spk, w.probs, s);
+  head_sortformer(w.x, B * W, m->h_w1t, m->h_b1, m->h_w2, m->h_b2, m->cfg.n_spk, w.probs, s);
 }
 
 static void encode_nemotron(const sf_model* m, EncWs& w, int B, int W, int n_valid,
                             hipStream_t s) {
   const bool bf = m->bf16;
-  const int M = B * W;
-  float* x = w.x;
+  Ctx c{m, w, B * W, s, bf};
+  c.ln(512, 0, nullptr, 0.f, m->rl[0].ln1_g, m->rl[0].ln1_b, nullptr, nullptr, 0, w.h);
   for (int l = 0; l < 31; ++l) {
     const TfLayer& L = m->rl[l];
-    layernorm(x, M, 512, L.ln1_g, L.ln1_b, nullptr, nullptr, nullptr, w.h, bf, s);
-    gemm_(w.h, 512, L.wqkv, 512, L.bqkv, M, 1536, 512, w.big, 1536, EPI_STORE, bf, bf, s);
+    c.qkv(w.h, 512, L.wqkv, L.bqkv, w.big, 64, W);
     AttnArgs a{};
-    a.qkv = w.big; a.ldq = 1536; a.qoff = 0; a.koff = 512; a.voff = 1024;
+    a.qkv = w.big; a.ldq = 1536; a.qoff = 0; a.koff = 512; a.vt = w.vt; a.vpitch = w.vpitch;
     a.B = B; a.H = 8; a.W = W; a.n_valid = n_valid; a.rope = m->rope;
     a.ctx = w.ctx; a.ldc = 512; a.scale = 0.125f;
     attention(a, ATT_ROPE, 64, bf, s);
-    gemm_(w.ctx, 512, L.wo, 512, L.bo, M, 512, 512, nullptr, 0, EPI_RESID, bf, false, s, x, 512,
-          1.f);
-    layernorm(x, M, 512, L.ln2_g, L.ln2_b, nullptr, nullptr, nullptr, w.h, bf, s);
-    gemm_(w.h, 512, L.w1, 512, L.b1, M, 2048, 512, w.big, 2048, EPI_GELU, bf, bf, s);
-    gemm_(w.big, 2048, L.w2, 2048, L.b2, M, 512, 2048, nullptr, 0, EPI_RESID, bf, false, s, x, 512,
-          1.f);
+    int ns = c.branch(w.ctx, 512, L.wo, 512, 512);
+    c.ln(512, ns, L.bo, 1.f, L.ln2_g, L.ln2_b, nullptr, nullptr, 1, w.h);   // pre-LN
+    c.lin(w.h, 512, L.w1, L.b1, 2048, 512, w.big, 2048, EPI_GELU, bf);
+    ns = c.branch(w.big, 2048, L.w2, 512, 2048);
+    if (l < 30)
+      c.ln(512, ns, L.b2, 1.f, m->rl[l + 1].ln1_g, m->rl[l + 1].ln1_b, nullptr, nullptr, 1, w.h);
+    else
+      c.ln(512, ns, L.b2, 1.f, m->fin_g, m->fin_b, nullptr, nullptr, 2, nullptr);  // final LN
   }
-  layernorm(x, M, 512, m->fin_g, m->fin_b, nullptr, nullptr, x, nullptr, bf, s);
-  head_nemotron(x, M, m->nh_w, m->nh_b, m->up_w, m->up_b, w.probs, w.probs10, s);
+  head_nemotron(w.x, B * W, m->nh_w, m->nh_b, m->up_w, m->up_b, w.probs, w.probs10, s);
 }
 
 void encode(const sf_model* m, EncWs& w, int B, int W, int n_valid, hipStream_t s) {

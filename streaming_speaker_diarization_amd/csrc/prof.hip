@@ -24,6 +24,8 @@ Prof& P() {
 }
 }  // namespace
 
+bool profiling() { return P().on; }
+
 bool prof_active(int cls) {
   Prof& p = P();
   return p.on && p.cls == cls && p.used + 2 <= p.ev.size();

@@ -31,7 +31,7 @@ class Model:
 
     def __del__(self):
         h = getattr(self, "handle", None)
-        if h:
+        if h and sf is not None and sf.sortformer_free is not None:
             sf.sortformer_free(h)
             self.handle = None
 
@@ -89,7 +89,7 @@ class Stream:
 
     def __del__(self):
         h = getattr(self, "handle", None)
-        if h:
+        if h and sf is not None and sf.sortformer_stream_destroy is not None:
             sf.sortformer_stream_destroy(h)
             self.handle = None
 

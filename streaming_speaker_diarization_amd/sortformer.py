@@ -31,7 +31,9 @@ EXPORTS = [
     "sortformer_encode_workspace_bytes", "sortformer_encode_window", "sortformer_pre_encode",
     "sortformer_pre_encode_workspace_bytes", "sortformer_config_num_tensors",
     "sortformer_config_tensor", "sortformer_profile_begin", "sortformer_profile_end",
+    "sortformer_stream_set_option",
 ]
+SF_STREAM_OPT_GRAPHS = 1
 SF_PROF = {"gemm": 1, "attn": 2, "ln": 3, "conv": 4, "frontend": 5, "cache": 6}
 
 
@@ -96,6 +98,7 @@ def load(path: str = LIB_PATH):
         "sortformer_config_num_tensors": (I32, [cfgp]),
         "sortformer_config_tensor": (I32, [cfgp, U64, I32, C.c_char_p, I32, C.POINTER(I64), P]),
         "sortformer_profile_begin": (I32, [I32, I32]),
+        "sortformer_stream_set_option": (I32, [P, I32, I32]),
         "sortformer_profile_end": (I32, [C.POINTER(C.c_double), C.POINTER(I64),
                                          C.POINTER(C.c_double), C.POINTER(C.c_double)]),
     }
@@ -226,6 +229,10 @@ def sortformer_stream_create(h, scfg, batch, d_state, stream=None):
 
 def sortformer_stream_destroy(st):
     load().sortformer_stream_destroy(st)
+
+
+def sortformer_stream_set_option(st, option, value):
+    _check(load().sortformer_stream_set_option(st, option, int(value)), "stream_set_option")
 
 
 def sortformer_stream_reset(st, stream=None):

@@ -262,3 +262,28 @@ def test_nemotron_1800s_vs_golden(nmbf):
     assert got.shape == ref.shape == (180000, 8)
     err, agree = _report("nemotron 1800 s bf16", got, ref)
     assert err <= 2e-2 and agree >= 0.995
+
+
+def test_graph_replays_match_direct_launches(rt, sf, sfbf):
+    """Window forwards replayed from captured HIP graphs equal the direct
+    launches bit for bit, on every replay (three passes, eager work and
+    synchronisations between them)."""
+    audio = _cuda(meeting_audio(25.0, 4, 81))[None]
+    st = sfbf.stream("low")
+    sf.sortformer_stream_set_option(st.handle, sf.SF_STREAM_OPT_GRAPHS, 0)
+    ref = st.run(audio).cpu().numpy()
+    sf.sortformer_stream_set_option(st.handle, sf.SF_STREAM_OPT_GRAPHS, 1)
+    for rep in range(3):
+        st.reset()
+        got = st.run(audio).cpu().numpy()
+        torch.cuda.synchronize()
+        _ = (torch.randn(1000, device="cuda") * 2).sum().item()   # eager work in between
+        assert np.array_equal(got, ref), f"replay {rep}"
+    b = sfbf.stream("ultra_low", batch=3)
+    a3 = _cuda(np.stack([meeting_audio(8.0, 2, 90 + i) for i in range(3)]))
+    sf.sortformer_stream_set_option(b.handle, sf.SF_STREAM_OPT_GRAPHS, 0)
+    r3 = b.run(a3).cpu().numpy()
+    sf.sortformer_stream_set_option(b.handle, sf.SF_STREAM_OPT_GRAPHS, 1)
+    for rep in range(2):
+        b.reset()
+        assert np.array_equal(b.run(a3).cpu().numpy(), r3), f"batched replay {rep}"
