@@ -113,7 +113,7 @@ void state_update(sf_stream* st, const float* probs, int W, int n_chunk, hipStre
 }
 
 void drop_graphs(sf_stream* st) {
-  for (auto& kv : st->graphs) hipGraphExecDestroy(static_cast<hipGraphExec_t>(kv.second));
+  for (auto& kv : st->graphs) (void)hipGraphExecDestroy(static_cast<hipGraphExec_t>(kv.second));
   st->graphs.clear();
 }
 
@@ -144,7 +144,7 @@ bool window_forward_graph(sf_stream* st, EncWs& enc, const void* ws, hipStream_t
     if (hipStreamEndCapture(cs, &g) != hipSuccess || !g) return false;
     hipGraphExec_t ex = nullptr;
     const bool ok = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0) == hipSuccess;
-    hipGraphDestroy(g);
+    (void)hipGraphDestroy(g);
     if (!ok) return false;
     it = st->graphs.emplace(key, ex).first;
   }
@@ -402,7 +402,7 @@ sf_status sortformer_stream_create(sf_model* m, const sf_stream_config* c, int32
 void sortformer_stream_destroy(sf_stream* st) {
   if (!st) return;
   drop_graphs(st);
-  if (st->cap_stream) hipStreamDestroy(static_cast<hipStream_t>(st->cap_stream));
+  if (st->cap_stream) (void)hipStreamDestroy(static_cast<hipStream_t>(st->cap_stream));
   delete st;
 }
 

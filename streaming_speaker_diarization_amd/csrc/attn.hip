@@ -1,13 +1,13 @@
 // Multi-head self-attention over one encoder window, flash-style.
 //
-// One single-wave workgroup = (16 query rows, head, stream), so a window of
-// a few hundred frames still spreads over a few hundred workgroups. Key/value
-// tiles of 64 frames are staged through LDS (V comes already transposed per
-// head from the QKV projection, so both MFMA operands are K-contiguous and
-// staging is plain 16-byte copies); the next tile's K, V (and position band)
-// are fetched into registers while the current tile is computed. Scores, the
-// online softmax (running max/sum in fp32, exp2 domain) and the P.V product
-// stay on the matrix cores and in registers.
+// One workgroup = 16 query rows of one (stream, head); its four waves take
+// the 64-frame key tiles round-robin (so a window of a few hundred frames
+// still spreads over many waves) and merge their online-softmax states at the
+// end. MFMA B operands (K rows, the relative-position band, V transposed per
+// head by the QKV projection) are read straight from global memory/L2 into
+// registers, the next tile's K and band while the current one is computed;
+// LDS only carries the score shift and the re-layout of P for P.V. Running
+// max/sum in fp32 in the exp2 domain; row reductions with DPP.
 //
 // Modes:
 //  ATT_RELPOS  FastConformer relative-position attention ("Streaming
@@ -15,9 +15,9 @@
 //    query i and key j is [(q_i+u).k_j + (q_i+v).p(i-j)]/sqrt(d). The
 //    projections p(delta) are input-independent and precomputed for every
 //    delta; per key tile the 80-row band of p that the tile's (i, j) pairs
-//    touch is staged in LDS, one more MFMA product G = (q+v).band^T is formed,
-//    and the shift is done by indexing G at column i-j+63 — no padded score
-//    matrix is materialised.
+//    touch feeds one more MFMA product G = (q+v).band^T, and the shift is done
+//    by indexing G (through LDS) at column i-j+63 — no padded score matrix is
+//    materialised.
 //  ATT_ROPE    rotary embedding on q and k (rotate-half, positions = window
 //    index, which restart at every chunk) for the Nemotron-style layers.
 //  ATT_PLAIN   standard scaled dot-product attention (transformer, d=24,
@@ -26,15 +26,6 @@
 #include "kernels.h"
 
 namespace sf {
-
-// A workgroup here is one wave: LDS writes by some lanes become visible to
-// the others once the wave's LDS operations have completed, so a wait on
-// the LDS counter replaces a workgroup barrier (whose fence would also drain
-// the prefetched global loads).
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt/expcnt unconstrained
-  __builtin_amdgcn_wave_barrier();
-}
 
 template <typename T> struct Pack;
 template <> struct Pack<float> {
@@ -49,43 +40,91 @@ template <> struct Pack<bf16_t> {
   }
 };
 
+// Fragment I/O: EPF consecutive elements (8 bf16 or 1 fp32) as one load.
+template <typename T> struct Frag;
+template <> struct Frag<bf16_t> {
+  typedef bf16x8_t type;
+  __device__ static type load(const bf16_t* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
+  __device__ static float get(const type& f, int e) {
+    return bf2f(__builtin_bit_cast(u16x8, f)[e]);
+  }
+  __device__ static type zero_if(const type& f, unsigned live_mask) {
+    u16x8 u = __builtin_bit_cast(u16x8, f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) u[e] = (live_mask >> e) & 1u ? u[e] : (uint16_t)0;
+    return __builtin_bit_cast(bf16x8_t, u);
+  }
+};
+template <> struct Frag<float> {
+  typedef float type;
+  __device__ static type load(const float* p) { return *p; }
+  __device__ static float get(const type& f, int) { return f; }
+  __device__ static type zero_if(const type& f, unsigned live_mask) { return live_mask & 1u ? f : 0.f; }
+};
+
+// Reductions over the 16 lanes of one MFMA row group with DPP (no LDS):
+// quad swaps (xor 1, xor 2), then rotations by 4 and 8 within the row.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false)));
+  return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+  return v;
+}
+
+// LDS hand-off between lanes of one wave (the producer and consumer are the
+// same wave, so waiting for its LDS operations is enough).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt/expcnt unconstrained
+  __builtin_amdgcn_wave_barrier();
+}
+
+// One workgroup = 16 query rows of one (stream, head); its 4 waves take the
+// key tiles (64 frames) round-robin and merge their partial softmax states at
+// the end. MFMA B operands are read straight from global memory (L2):
+//  K rows   [key][dim]          -> scores  S = Q K^T
+//  p band   [delta][dim]        -> G = (q+v) p(delta)^T  (relative position)
+//  V^T rows [dim][key]          -> O += P V
+// so the only LDS traffic is the score shift (G) and the re-layout of P.
 template <typename T, int HD, int MODE>
-__global__ __launch_bounds__(64) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   using M_ = MF<T>;
+  using F = Frag<T>;
+  typedef typename F::type frag_t;
   constexpr int KI = M_::KI;
-  constexpr int EPF = KI / 4;              // elements per fragment per lane
-  constexpr int HDP = HD <= 32 ? 32 : 64;  // padded head dim
-  constexpr int VEC = 16 / (int)sizeof(T);
-  constexpr int LDK = HDP + VEC;
-  constexpr int LDV = 64 + VEC;
-  constexpr int NQF = HDP / KI;
-  constexpr int CPR = HDP / VEC;           // 16-byte chunks per staged row
+  constexpr int EPF = KI / 4;              // consecutive elements per fragment
+  constexpr int HDP = HD <= 32 ? 32 : 64;  // head dim padded for MFMA
+  constexpr int NQF = HDP / KI;            // k-steps over head dims
+  constexpr int NKF = 64 / KI;             // k-steps over a 64-key tile
+  constexpr int NDT = HDP / 16;            // output column tiles
+  constexpr int LDP = 64 + 16 / (int)sizeof(T);
   constexpr bool REL = MODE == ATT_RELPOS;
   constexpr bool ROPE = MODE == ATT_ROPE;
   static_assert(!ROPE || HD == 64, "rotary layers use 64-dim heads");
-  constexpr int NB = 80;                   // band rows: 16 queries + 64 keys - 1, padded
-  constexpr int KCH = ROPE ? 64 * (CPR / 2) / 64 : 64 * CPR / 64;  // K chunks (pairs) per lane
-  constexpr int VCPR = 64 / VEC;           // chunks per V^T row (64 keys)
-  constexpr int VCH = HDP * VCPR / 64;
-  constexpr int BCH = REL ? NB * CPR / 64 : 1;
-  __shared__ __align__(16) T Ks[64 * LDK];
-  __shared__ __align__(16) T Vt[HDP * LDV];
-  __shared__ __align__(16) T Pb[REL ? NB * LDK : VEC];
-  __shared__ float Gs[REL ? 16 * 81 : 1];
-  __shared__ __align__(16) T Ps[16 * LDV];
+  __shared__ float Gs[REL ? 4 * 16 * 81 : 1];
+  __shared__ __align__(16) T Ps[4 * 16 * LDP];
+  __shared__ float Ms[4][16], Ls[4][16];
+  __shared__ float Os[4][16][HDP + 1];
 
-  const int lane = threadIdx.x, g = lane >> 4, c16 = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c16 = lane & 15;
   const int iq0 = blockIdx.x * 16, h = blockIdx.y, b = blockIdx.z;
   const T* qkv = static_cast<const T*>(a.qkv);
   const size_t rowbase = (size_t)b * a.W;
   const float sl2 = a.scale * 1.4426950408889634f;
+  const T* vtb = static_cast<const T*>(a.vt) + (size_t)(b * a.H + h) * HD * a.vpitch;
 
-  // ---- query fragments for row iq0+c16: element e of fragment ks is dim
-  // ks*KI + EPF*g + e.
-  typename M_::frag qa[NQF], qb[NQF];
+  // ---- query fragments for row iq0+c16 (element e of fragment ks is dim
+  // ks*KI + EPF*g + e)
+  frag_t qa[NQF], qb[NQF];
   {
-    const int qi = iq0 + c16;
-    const int qc = min(qi, a.W - 1);
+    const int qi = iq0 + c16, qc = min(qi, a.W - 1);
     float q[NQF][EPF];
 #pragma unroll
     for (int ks = 0; ks < NQF; ++ks)
@@ -103,13 +142,12 @@ __global__ __launch_bounds__(64) void attn_kernel(AttnArgs a) {
       }
     if constexpr (ROPE) {
       constexpr int HALF = 32 / KI;  // fragment offset of dim d+32
-      const int pos = qi < a.W ? qi : 0;
 #pragma unroll
       for (int ks = 0; ks < HALF; ++ks)
 #pragma unroll
         for (int e = 0; e < EPF; ++e) {
           const int d = ks * KI + EPF * g + e;
-          const float c = a.rope[(pos * 32 + d) * 2], s = a.rope[(pos * 32 + d) * 2 + 1];
+          const float c = a.rope[(qc * 32 + d) * 2], s = a.rope[(qc * 32 + d) * 2 + 1];
           const float x1 = q[ks][e], x2 = q[ks + HALF][e];
           q[ks][e] = x1 * c - x2 * s;
           q[ks + HALF][e] = x2 * c + x1 * s;
@@ -133,150 +171,121 @@ __global__ __launch_bounds__(64) void attn_kernel(AttnArgs a) {
       qb[ks] = Pack<T>::make(va);
     }
   }
+  // live-dimension mask of this lane's fragment elements for each k-step
+  auto dim_mask = [&](int ks) {
+    unsigned m = 0;
+#pragma unroll
+    for (int e = 0; e < EPF; ++e) m |= (ks * KI + EPF * g + e < HD ? 1u : 0u) << e;
+    return m;
+  };
 
-  // ---- register staging of one key tile (K, V and the position band); the
-  // next tile is fetched while the current one is being computed.
-  const vec16 zero{{0u, 0u, 0u, 0u}};
-  vec16 kr[KCH], kr2[ROPE ? KCH : 1], vr[VCH], br[BCH];
-  // Loads are unconditional (clamped rows/chunks) so they all issue back to
-  // back; out-of-range chunks are zeroed by the selects in `mask`.
-  auto fetch = [&](int j0) {
+  frag_t kf[4][NQF], bfr[REL ? 5 : 1][NQF], vf[NDT][NKF];
+  // K and position-band fragments of key tile j0 (issued together)
+  auto load_kb = [&](int j0) {
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int idx = lane + 64 * i;
-      const int r = ROPE ? idx / (CPR / 2) : idx / CPR, c = ROPE ? idx % (CPR / 2) : idx % CPR;
-      const int j = min(j0 + r, a.W - 1), d0 = min(c * VEC, HD - VEC);
-      const size_t base = (rowbase + j) * a.ldq + a.koff + h * HD + d0;
-      kr[i] = *reinterpret_cast<const vec16*>(qkv + base);
-      if constexpr (ROPE) kr2[i] = *reinterpret_cast<const vec16*>(qkv + base + 32);
-    }
-    const T* vt = static_cast<const T*>(a.vt) + (size_t)(b * a.H + h) * HD * a.vpitch;
+    for (int nt = 0; nt < 4; ++nt) {
+      const int j = min(j0 + 16 * nt + c16, a.W - 1);
+      const T* kr = qkv + (rowbase + j) * a.ldq + a.koff + h * HD;
 #pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int idx = lane + 64 * i, d = min(idx / VCPR, HD - 1);
-      const int k0 = min(j0 + (idx % VCPR) * VEC, a.vpitch - VEC);
-      vr[i] = *reinterpret_cast<const vec16*>(vt + (size_t)d * a.vpitch + k0);
+      for (int ks = 0; ks < NQF; ++ks) kf[nt][ks] = F::load(kr + min(ks * KI + EPF * g, HD - EPF));
     }
     if constexpr (REL) {
       const int dbase = iq0 - j0 - 63 + a.p_center;
 #pragma unroll
-      for (int i = 0; i < BCH; ++i) {
-        const int idx = lane + 64 * i, r = idx / CPR, d0 = min((idx % CPR) * VEC, HD - VEC);
-        const int trow = min(max(dbase + r, 0), 2 * a.p_center);
-        br[i] = *reinterpret_cast<const vec16*>(static_cast<const T*>(a.P) + (size_t)trow * a.ldp +
-                                                h * HD + d0);
+      for (int ct = 0; ct < 5; ++ct) {
+        const int tr = min(max(dbase + 16 * ct + c16, 0), 2 * a.p_center);
+        const T* pr = static_cast<const T*>(a.P) + (size_t)tr * a.ldp + h * HD;
+#pragma unroll
+        for (int ks = 0; ks < NQF; ++ks) bfr[ct][ks] = F::load(pr + min(ks * KI + EPF * g, HD - EPF));
       }
     }
   };
-  auto zap = [](vec16& v, bool live) {
+  auto load_v = [&](int j0) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) v.w[q] = live ? v.w[q] : 0u;
-  };
-  auto mask = [&](int j0) {
+    for (int dt = 0; dt < NDT; ++dt) {
+      const T* vr = vtb + (size_t)min(16 * dt + c16, HD - 1) * a.vpitch;
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int idx = lane + 64 * i;
-      const int r = ROPE ? idx / (CPR / 2) : idx / CPR, c = ROPE ? idx % (CPR / 2) : idx % CPR;
-      zap(kr[i], j0 + r < a.W && c * VEC < HD);
-      if constexpr (ROPE) zap(kr2[i], j0 + r < a.W);
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {  // dims past HD and keys past W are zero
-      const int idx = lane + 64 * i, k0 = j0 + (idx % VCPR) * VEC;
-      T* ve = reinterpret_cast<T*>(&vr[i]);
-      const bool dl = idx / VCPR < HD && k0 + VEC <= a.vpitch;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) ve[e] = (dl && k0 + e < a.W) ? ve[e] : from_f<T>(0.f);
-    }
-    if constexpr (REL) {
-      const int dbase = iq0 - j0 - 63 + a.p_center;
-#pragma unroll
-      for (int i = 0; i < BCH; ++i) {
-        const int idx = lane + 64 * i, trow = dbase + idx / CPR;
-        zap(br[i], trow >= 0 && trow <= 2 * a.p_center && (idx % CPR) * VEC < HD);
-      }
-    }
-  };
-  auto stash = [&](int j0) {
-    mask(j0);
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int idx = lane + 64 * i;
-      const int r = ROPE ? idx / (CPR / 2) : idx / CPR, c = ROPE ? idx % (CPR / 2) : idx % CPR;
-      const int d0 = c * VEC;
-      if constexpr (ROPE) {
-        const T* k1e = reinterpret_cast<const T*>(&kr[i]);
-        const T* k2e = reinterpret_cast<const T*>(&kr2[i]);
-        const int pos = j0 + r < a.W ? j0 + r : 0;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          const float c_ = a.rope[(pos * 32 + d0 + e) * 2], s_ = a.rope[(pos * 32 + d0 + e) * 2 + 1];
-          const float x1 = to_f<T>(k1e[e]), x2 = to_f<T>(k2e[e]);
-          Ks[r * LDK + d0 + e] = from_f<T>(x1 * c_ - x2 * s_);
-          Ks[r * LDK + d0 + 32 + e] = from_f<T>(x2 * c_ + x1 * s_);
-        }
-      } else {
-        *reinterpret_cast<vec16*>(&Ks[r * LDK + d0]) = kr[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int idx = lane + 64 * i;
-      *reinterpret_cast<vec16*>(&Vt[(idx / VCPR) * LDV + (idx % VCPR) * VEC]) = vr[i];
-    }
-    if constexpr (REL) {
-#pragma unroll
-      for (int i = 0; i < BCH; ++i) {
-        const int idx = lane + 64 * i, r = idx / CPR, d0 = (idx % CPR) * VEC;
-        *reinterpret_cast<vec16*>(&Pb[r * LDK + d0]) = br[i];
-      }
+      for (int ks = 0; ks < NKF; ++ks)
+        vf[dt][ks] = F::load(vr + min(j0 + ks * KI + EPF * g, a.vpitch - EPF));
     }
   };
 
-  f32x4 O[HDP / 16];
+  f32x4 O[NDT];
 #pragma unroll
-  for (int dt = 0; dt < HDP / 16; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int dt = 0; dt < NDT; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float mrow[4], lrow[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) { mrow[r] = -INFINITY; lrow[r] = 0.f; }
 
   const int ntile = (a.n_valid + 63) / 64;
-  fetch(0);
-  for (int kt = 0; kt < ntile; ++kt) {
+  if (w < ntile) load_kb(w * 64);
+  for (int kt = w; kt < ntile; kt += 4) {
     const int j0 = kt * 64;
-    wave_lds_sync();
-    stash(j0);
-    wave_lds_sync();
-    if (kt + 1 < ntile) fetch(j0 + 64);
-
+    load_v(j0);
+    // the loads are unconditional: zero what lies outside the head / window
+#pragma unroll
+    for (int ks = 0; ks < NQF; ++ks) {
+      const unsigned dm = dim_mask(ks);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) kf[nt][ks] = F::zero_if(kf[nt][ks], dm);
+      if constexpr (REL) {
+        const int dbase = iq0 - j0 - 63;
+#pragma unroll
+        for (int ct = 0; ct < 5; ++ct) {
+          const int dl = dbase + 16 * ct + c16;
+          bfr[ct][ks] = F::zero_if(bfr[ct][ks], (dl >= -a.p_center && dl <= a.p_center) ? dm : 0u);
+        }
+      }
+    }
+    if constexpr (ROPE) {  // rotate the keys (positions = window index)
+      constexpr int HALF = 32 / KI;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int pos = min(j0 + 16 * nt + c16, a.W - 1);
+#pragma unroll
+        for (int ks = 0; ks < HALF; ++ks) {
+          float x1[EPF], x2[EPF];
+#pragma unroll
+          for (int e = 0; e < EPF; ++e) {
+            const int d = ks * KI + EPF * g + e;
+            const float c = a.rope[(pos * 32 + d) * 2], s = a.rope[(pos * 32 + d) * 2 + 1];
+            const float k1 = F::get(kf[nt][ks], e), k2 = F::get(kf[nt][ks + HALF], e);
+            x1[e] = k1 * c - k2 * s;
+            x2[e] = k2 * c + k1 * s;
+          }
+          kf[nt][ks] = Pack<T>::make(x1);
+          kf[nt][ks + HALF] = Pack<T>::make(x2);
+        }
+      }
+    }
     // ---- scores
     f32x4 S[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       S[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < NQF; ++ks)
-        S[nt] = M_::mma(qa[ks], M_::ld(&Ks[(16 * nt + c16) * LDK + ks * KI], lane), S[nt]);
+      for (int ks = 0; ks < NQF; ++ks) S[nt] = M_::mma(qa[ks], kf[nt][ks], S[nt]);
     }
     if constexpr (REL) {
-      // G[i][c] = (q_i+v).band[c], band row c <-> relative distance
-      // iq0-j0-63+c; the score of (i, j) takes column i-j+63.
+      // G[i][c] = (q_i+v).p(delta_c), band row c <-> delta iq0-j0-63+c; the
+      // score of (i, j) takes column i-j+63.
+      float* G = &Gs[w * 16 * 81];
 #pragma unroll
       for (int ct = 0; ct < 5; ++ct) {
         f32x4 acc{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < NQF; ++ks)
-          acc = M_::mma(qb[ks], M_::ld(&Pb[(16 * ct + c16) * LDK + ks * KI], lane), acc);
+        for (int ks = 0; ks < NQF; ++ks) acc = M_::mma(qb[ks], bfr[ct][ks], acc);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Gs[(4 * g + r) * 81 + 16 * ct + c16] = acc[r];
+        for (int r = 0; r < 4; ++r) G[(4 * g + r) * 81 + 16 * ct + c16] = acc[r];
       }
       wave_lds_sync();
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          S[nt][r] += Gs[(4 * g + r) * 81 + (4 * g + r) - (16 * nt + c16) + 63];
+          S[nt][r] += G[(4 * g + r) * 81 + (4 * g + r) - (16 * nt + c16) + 63];
     }
+    if (kt + 4 < ntile) load_kb(j0 + 256);  // next tile of this wave, in flight now
 
     // ---- online softmax (log2 domain)
     float mx[4];
@@ -291,53 +300,75 @@ __global__ __launch_bounds__(64) void attn_kernel(AttnArgs a) {
         mx[r] = fmaxf(mx[r], S[nt][r]);
       }
     }
+    T* Pw = &Ps[w * 16 * LDP];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float mnew = fmaxf(mrow[r], group16_max(mx[r]));
+      const float mnew = fmaxf(mrow[r], row16_max(mx[r]));
       const float alpha = exp2f(mrow[r] - mnew);
       float rs = 0.f;
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         const float p = exp2f(S[nt][r] - mnew);
         rs += p;
-        Ps[(4 * g + r) * LDV + 16 * nt + c16] = from_f<T>(p);
+        Pw[(4 * g + r) * LDP + 16 * nt + c16] = from_f<T>(p);
       }
-      lrow[r] = lrow[r] * alpha + group16_sum(rs);
+      lrow[r] = lrow[r] * alpha + row16_sum(rs);
       mrow[r] = mnew;
 #pragma unroll
-      for (int dt = 0; dt < HDP / 16; ++dt) O[dt][r] *= alpha;
+      for (int dt = 0; dt < NDT; ++dt) O[dt][r] *= alpha;
     }
     wave_lds_sync();
-    // ---- O += P.V
+    // ---- O += P.V (V^T columns past the window or the head are zero)
 #pragma unroll
-    for (int dt = 0; dt < HDP / 16; ++dt)
+    for (int ks = 0; ks < NKF; ++ks) {
+      unsigned km = 0;
 #pragma unroll
-      for (int ks = 0; ks < 64 / KI; ++ks)
-        O[dt] = M_::mma(M_::ld(&Ps[c16 * LDV + ks * KI], lane),
-                        M_::ld(&Vt[(16 * dt + c16) * LDV + ks * KI], lane), O[dt]);
+      for (int e = 0; e < EPF; ++e) km |= (j0 + ks * KI + EPF * g + e < a.W ? 1u : 0u) << e;
+      const auto pa = M_::ld(&Pw[c16 * LDP + ks * KI], lane);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        O[dt] = M_::mma(pa, F::zero_if(vf[dt][ks], 16 * dt + c16 < HD ? km : 0u), O[dt]);
+    }
   }
 
+  // ---- merge the four waves' partial softmax states
+  if (c16 == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) { Ms[w][4 * g + r] = mrow[r]; Ls[w][4 * g + r] = lrow[r]; }
+  }
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Os[w][4 * g + r][16 * dt + c16] = O[dt][r];
+  __syncthreads();
   T* ctx = static_cast<T*>(a.ctx);
+  for (int o = tid; o < 16 * HD; o += 256) {
+    const int r = o / HD, d = o % HD, i = iq0 + r;
+    float mx = Ms[0][r];
 #pragma unroll
-  for (int dt = 0; dt < HDP / 16; ++dt)
+    for (int v = 1; v < 4; ++v) mx = fmaxf(mx, Ms[v][r]);
+    float l = 0.f, acc = 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = iq0 + 4 * g + r, d = 16 * dt + c16;
-      if (i < a.W && d < HD) ctx[(rowbase + i) * a.ldc + h * HD + d] = from_f<T>(O[dt][r] / lrow[r]);
+    for (int v = 0; v < 4; ++v) {
+      const float f = exp2f(Ms[v][r] - mx);  // waves without tiles: exp2(-inf) = 0
+      l += Ls[v][r] * f;
+      acc += Os[v][r][d] * f;
     }
+    if (i < a.W) ctx[(rowbase + i) * a.ldc + h * HD + d] = from_f<T>(acc / l);
+  }
 }
 
 template <typename T>
-static void launch_attn(const AttnArgs& a, int mode, int hd, hipStream_t s) {
-  dim3 grid((a.W + 15) / 16, a.H, a.B);
+static void launch_attn(const AttnArgs& a, int mode, int hd, hipStream_t s, double fl, double by) {
+  dim3 grid((a.W + 15) / 16, a.H, a.B);  // 4 waves per 16 query rows
   if (mode == ATT_RELPOS && hd == 64)
-    hipLaunchKernelGGL((attn_kernel<T, 64, ATT_RELPOS>), grid, dim3(64), 0, s, a);
+    klaunch(PROF_ATTN, fl, by, attn_kernel<T, 64, ATT_RELPOS>, grid, dim3(256), s, a);
   else if (mode == ATT_ROPE && hd == 64)
-    hipLaunchKernelGGL((attn_kernel<T, 64, ATT_ROPE>), grid, dim3(64), 0, s, a);
+    klaunch(PROF_ATTN, fl, by, attn_kernel<T, 64, ATT_ROPE>, grid, dim3(256), s, a);
   else if (mode == ATT_PLAIN && hd == 24)
-    hipLaunchKernelGGL((attn_kernel<T, 24, ATT_PLAIN>), grid, dim3(64), 0, s, a);
+    klaunch(PROF_ATTN, fl, by, attn_kernel<T, 24, ATT_PLAIN>, grid, dim3(256), s, a);
   else if (mode == ATT_PLAIN && hd == 64)
-    hipLaunchKernelGGL((attn_kernel<T, 64, ATT_PLAIN>), grid, dim3(64), 0, s, a);
+    klaunch(PROF_ATTN, fl, by, attn_kernel<T, 64, ATT_PLAIN>, grid, dim3(256), s, a);
 }
 
 void attention(const AttnArgs& a, int mode, int head_dim, bool bf16, hipStream_t s) {
@@ -345,10 +376,10 @@ void attention(const AttnArgs& a, int mode, int head_dim, bool bf16, hipStream_t
   // scores (q.k), the relative-position term (q.p(i-j)) and P.V per head
   const double pairs = (double)a.B * a.H * a.W * a.n_valid;
   const double es = bf16 ? 2 : 4;
-  ProfScope ps(PROF_ATTN, s, pairs * 2.0 * head_dim * (mode == ATT_RELPOS ? 3 : 2),
-               es * a.B * a.W * a.H * head_dim * 4.0);
-  if (bf16) launch_attn<bf16_t>(a, mode, head_dim, s);
-  else launch_attn<float>(a, mode, head_dim, s);
+  const double fl = pairs * 2.0 * head_dim * (mode == ATT_RELPOS ? 3 : 2);
+  const double by = es * a.B * a.W * a.H * head_dim * 4.0;
+  if (bf16) launch_attn<bf16_t>(a, mode, head_dim, s, fl, by);
+  else launch_attn<float>(a, mode, head_dim, s, fl, by);
 }
 
 }  // namespace sf

@@ -118,11 +118,11 @@ __global__ __launch_bounds__(128) void cache_gather_kernel(const float* E, const
 void compress_cache(const float* E, const float* P, const int* ph, int cap, int D, int S, int B,
                     int M, int tail, const double* sil_sum, const int* sil_cnt, int C, int per,
                     int k, float* E2, float* P2, int* ph2, int* slots, hipStream_t s) {
-  ProfScope ps(PROF_CACHE, s, 0.0, (double)B * ((double)M * (S + 1) * 4 + (double)(C + tail) * (D + S + 1) * 8));
-  hipLaunchKernelGGL(compress_kernel, dim3(B), dim3(512), 0, s, E, P, ph, cap, D, S, M, tail,
-                     sil_sum, sil_cnt, C, per, k, slots);
-  hipLaunchKernelGGL(cache_gather_kernel, dim3(C + tail, B), dim3(128), 0, s, E, P, ph, cap, D, S,
-                     M, C, slots, sil_sum, sil_cnt, E2, P2, ph2);
+  klaunch(PROF_CACHE, 0.0, (double)B * M * (S + 1) * 4, compress_kernel, dim3(B), dim3(512), s, E,
+          P, ph, cap, D, S, M, tail, sil_sum, sil_cnt, C, per, k, slots);
+  klaunch(PROF_CACHE, 0.0, (double)B * (C + tail) * (D + S + 1) * 8, cache_gather_kernel,
+          dim3(C + tail, B), dim3(128), s, E, P, ph, cap, D, S, M, C, (const int*)slots, sil_sum,
+          sil_cnt, E2, P2, ph2);
 }
 
 }  // namespace sf

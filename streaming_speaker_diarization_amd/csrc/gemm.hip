@@ -84,7 +84,24 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x4 (&acc)[TM][TN]
             float* part = static_cast<float*>(g.out);
             part[((size_t)split * g.M + m) * g.N + n] = acc[i][j][r];
           } else if constexpr (EPI == EPI_QKV) {
-            qkv_store<OutT>(g, m, n, acc[i][j][r] + bn);
+            if (n < g.vcol || sizeof(OutT) != 2) {
+              qkv_store<OutT>(g, m, n, acc[i][j][r] + bn);
+            } else if (r == 0) {
+              // rows m..m+3 of one V column are 4 consecutive keys of V^T
+              const int nn = n - g.vcol, hh = nn / g.vhd, d = nn % g.vhd;
+              const int bb = m / g.vrows, w0 = m % g.vrows, H = (g.N - g.vcol) / g.vhd;
+              if (m + 3 < g.M && w0 + 3 < g.vrows && (w0 & 3) == 0) {
+                uint2 pk;
+                pk.x = (uint32_t)f2bf(acc[i][j][0] + bn) | ((uint32_t)f2bf(acc[i][j][1] + bn) << 16);
+                pk.y = (uint32_t)f2bf(acc[i][j][2] + bn) | ((uint32_t)f2bf(acc[i][j][3] + bn) << 16);
+                *reinterpret_cast<uint2*>(static_cast<bf16_t*>(g.vt) +
+                                          ((size_t)(bb * H + hh) * g.vhd + d) * g.vpitch + w0) = pk;
+              } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                  if (m + q < g.M) qkv_store<OutT>(g, m + q, n, acc[i][j][q] + bn);
+              }
+            }
           } else {
             epi_store<EPI, OutT>(g, m, n, acc[i][j][r] + bn);
           }
@@ -284,10 +301,13 @@ static int n_slices(int K) {
   return ns;
 }
 
+// algorithmic work of the gemm() call being launched (for profiling)
+static thread_local double g_flops = 0, g_bytes = 0;
+
 template <typename T, typename OutT, int EPI, int KS>
 static void slice_launch(const GemmArgs& g, int ns, hipStream_t s) {
   dim3 grid(g.N / 64, (g.M + 63) / 64, ns);
-  hipLaunchKernelGGL((gemm_slice_kernel<T, OutT, EPI, KS>), grid, dim3(256), 0, s, g);
+  klaunch(PROF_GEMM, g_flops, g_bytes, gemm_slice_kernel<T, OutT, EPI, KS>, grid, dim3(256), s, g);
 }
 
 template <typename T, typename OutT, int EPI>
@@ -307,10 +327,12 @@ static void launch_kernel(const GemmArgs& g, int ns, hipStream_t s) {
     }
   } else if (g.M > 1536 && g.N % 128 == 0) {
     dim3 grid(g.N / 128, (g.M + 127) / 128, ns);
-    hipLaunchKernelGGL((gemm_loop_kernel<T, OutT, 128, 128, EPI>), grid, dim3(256), 0, s, g, ks);
+    klaunch(PROF_GEMM, g_flops, g_bytes, gemm_loop_kernel<T, OutT, 128, 128, EPI>, grid, dim3(256), s,
+            g, ks);
   } else {
     dim3 grid(g.N / 64, (g.M + 63) / 64, ns);
-    hipLaunchKernelGGL((gemm_loop_kernel<T, OutT, 64, 64, EPI>), grid, dim3(256), 0, s, g, ks);
+    klaunch(PROF_GEMM, g_flops, g_bytes, gemm_loop_kernel<T, OutT, 64, 64, EPI>, grid, dim3(256), s,
+            g, ks);
   }
 }
 
@@ -326,8 +348,9 @@ static int launch(const GemmArgs& g, hipStream_t s) {
   GemmArgs p = g;
   p.out = g.part;
   launch_kernel<T, float, EPI_PARTIAL>(p, ns, s);
-  hipLaunchKernelGGL((splitk_epi_kernel<OutT, EPI>), dim3(g.M), dim3(256), 0, s, g,
-                     static_cast<const float*>(g.part), ns);
+  g_flops = g_bytes = 0;  // the reduction launch carries no extra algorithmic work
+  klaunch(PROF_GEMM, 0.0, 0.0, splitk_epi_kernel<OutT, EPI>, dim3(g.M), dim3(256), s, g,
+          static_cast<const float*>(g.part), ns);
   return 1;
 }
 
@@ -366,8 +389,8 @@ int gemm(const GemmArgs& g, int epi, bool bf16_in, bool bf16_out, hipStream_t s)
   if (g.M <= 0) return 1;
   const double ie = bf16_in ? 2 : 4, oe = (epi == EPI_PARTIAL) ? 4 : (bf16_out ? 2 : 4);
   const double on = epi == EPI_GLU ? 0.5 : 1.0;
-  ProfScope ps(PROF_GEMM, s, 2.0 * g.M * g.N * g.K,
-               ie * ((double)g.M * g.K + (double)g.N * g.K) + oe * on * g.M * g.N);
+  g_flops = 2.0 * g.M * g.N * g.K;
+  g_bytes = ie * ((double)g.M * g.K + (double)g.N * g.K) + oe * on * g.M * g.N;
   if (epi == EPI_PARTIAL)
     return checked(bf16_in ? launch<bf16_t, float, EPI_PARTIAL>(g, s)
                            : launch<float, float, EPI_PARTIAL>(g, s));

@@ -1,6 +1,8 @@
 // Launch interfaces of the gfx950 kernels. Every launcher only enqueues on
 // the given stream; shapes are validated by the host code that calls them.
 #pragma once
+#include <hip/hip_ext.h>
+
 #include "common.h"
 
 namespace sf {
@@ -104,24 +106,26 @@ void compress_cache(const float* E, const float* P, const int* ph, int cap, int 
 // Benchmark profiling (see prof.hip). Classes match SF_PROF_* in the ABI.
 enum { PROF_GEMM = 1, PROF_ATTN = 2, PROF_LN = 3, PROF_CONV = 4, PROF_FRONTEND = 5, PROF_CACHE = 6 };
 bool prof_active(int cls);
-void prof_begin_launch(hipStream_t s);
-void prof_end_launch(hipStream_t s, double flops, double bytes);
+// Next event pair of the pool (and the launch's algorithmic flops/bytes).
+void prof_next(hipEvent_t* start, hipEvent_t* stop, double flops, double bytes);
 int prof_start(int cls, int max_launches);
 int prof_stop(double* ms, long long* launches, double* flops, double* bytes);
 bool profiling();  // any class being profiled (graph capture is then bypassed)
 
-// Brackets one launch with profiling events when its class is being profiled.
-struct ProfScope {
-  bool on;
-  hipStream_t s;
-  double f, b;
-  ProfScope(int cls, hipStream_t st, double flops, double bytes)
-      : on(prof_active(cls)), s(st), f(flops), b(bytes) {
-    if (on) prof_begin_launch(s);
+// Launches a kernel; while its class is profiled the launch carries a start
+// and a stop event recorded by the dispatch itself, so the timed interval is
+// exactly the kernel's execution.
+// Arguments are converted to the kernel's parameter types before packing.
+template <typename... KArgs, typename... Args>
+inline void klaunch(int cls, double flops, double bytes, void (*kern)(KArgs...), dim3 grid,
+                    dim3 block, hipStream_t s, Args... args) {
+  if (prof_active(cls)) {
+    hipEvent_t e0, e1;
+    prof_next(&e0, &e1, flops, bytes);
+    hipExtLaunchKernelGGL(kern, grid, block, 0, s, e0, e1, 0, static_cast<KArgs>(args)...);
+  } else {
+    hipLaunchKernelGGL(kern, grid, block, 0, s, static_cast<KArgs>(args)...);
   }
-  ~ProfScope() {
-    if (on) prof_end_launch(s, f, b);
-  }
-};
+}
 
 }  // namespace sf

@@ -65,14 +65,14 @@ __global__ __launch_bounds__(256) void ln_kernel(LnArgs a) {
 }
 
 template <typename T, int D>
-static void ln_launch(const LnArgs& a, dim3 grid, hipStream_t s) {
+static void ln_launch(const LnArgs& a, dim3 grid, hipStream_t s, double by) {
   switch (a.part ? a.nsplit : 0) {
-    case 0: hipLaunchKernelGGL((ln_kernel<T, D, 0>), grid, dim3(256), 0, s, a); break;
-    case 1: hipLaunchKernelGGL((ln_kernel<T, D, 1>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((ln_kernel<T, D, 2>), grid, dim3(256), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((ln_kernel<T, D, 3>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((ln_kernel<T, D, 4>), grid, dim3(256), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((ln_kernel<T, D, 8>), grid, dim3(256), 0, s, a); break;
+    case 0: klaunch(PROF_LN, 0.0, by, ln_kernel<T, D, 0>, grid, dim3(256), s, a); break;
+    case 1: klaunch(PROF_LN, 0.0, by, ln_kernel<T, D, 1>, grid, dim3(256), s, a); break;
+    case 2: klaunch(PROF_LN, 0.0, by, ln_kernel<T, D, 2>, grid, dim3(256), s, a); break;
+    case 3: klaunch(PROF_LN, 0.0, by, ln_kernel<T, D, 3>, grid, dim3(256), s, a); break;
+    case 4: klaunch(PROF_LN, 0.0, by, ln_kernel<T, D, 4>, grid, dim3(256), s, a); break;
+    case 8: klaunch(PROF_LN, 0.0, by, ln_kernel<T, D, 8>, grid, dim3(256), s, a); break;
     default: break;  // rejected by layernorm()
   }
 }
@@ -84,16 +84,15 @@ void layernorm(const LnArgs& a, bool bf16, hipStream_t s) {
     flag_launch_failure();
     return;
   }
-  ProfScope ps(PROF_LN, s, 0.0,
-               (double)a.M * a.D * (4.0 + 4.0 * ns + (a.x_mode ? 4.0 : 0.0) +
-                                    (a.y_act ? (bf16 ? 2.0 : 4.0) : 0.0)));
+  const double by = (double)a.M * a.D * (4.0 + 4.0 * ns + (a.x_mode ? 4.0 : 0.0) +
+                                           (a.y_act ? (bf16 ? 2.0 : 4.0) : 0.0));
   dim3 grid((a.M + 3) / 4);
   if (bf16) {
-    if (a.D == 512) ln_launch<bf16_t, 512>(a, grid, s);
-    else ln_launch<bf16_t, 192>(a, grid, s);
+    if (a.D == 512) ln_launch<bf16_t, 512>(a, grid, s, by);
+    else ln_launch<bf16_t, 192>(a, grid, s, by);
   } else {
-    if (a.D == 512) ln_launch<float, 512>(a, grid, s);
-    else ln_launch<float, 192>(a, grid, s);
+    if (a.D == 512) ln_launch<float, 512>(a, grid, s, by);
+    else ln_launch<float, 192>(a, grid, s, by);
   }
 }
 
@@ -129,14 +128,14 @@ __global__ __launch_bounds__(256) void dwconv_time_kernel(const float* glu, int 
 void dwconv_time(const float* glu, int B, int W, int n_valid, const float* w9, const float* sc,
                  const float* sh, void* out, bool bf16, hipStream_t s) {
   if (W <= 0) return;
-  ProfScope ps(PROF_CONV, s, 2.0 * 9 * 512 * B * W, (double)B * W * 512 * (4.0 + (bf16 ? 2 : 4)));
+  const double fl = 2.0 * 9 * 512 * B * W, by = (double)B * W * 512 * (4.0 + (bf16 ? 2 : 4));
   dim3 grid(W, B);
   if (bf16)
-    hipLaunchKernelGGL((dwconv_time_kernel<bf16_t>), grid, dim3(256), 0, s, glu, W, n_valid, w9,
-                       sc, sh, static_cast<bf16_t*>(out));
+    klaunch(PROF_CONV, fl, by, dwconv_time_kernel<bf16_t>, grid, dim3(256), s, glu, W, n_valid, w9,
+            sc, sh, static_cast<bf16_t*>(out));
   else
-    hipLaunchKernelGGL((dwconv_time_kernel<float>), grid, dim3(256), 0, s, glu, W, n_valid, w9, sc,
-                       sh, static_cast<float*>(out));
+    klaunch(PROF_CONV, fl, by, dwconv_time_kernel<float>, grid, dim3(256), s, glu, W, n_valid, w9,
+            sc, sh, static_cast<float*>(out));
 }
 
 // ------------------------------------------------------------ log-mel
@@ -208,11 +207,10 @@ void logmel(const float* audio, long long a_bstride, long long ring_mask, long l
             long long t0, int nfr, int B, const float* tab, float* mel, long long m_bstride,
             hipStream_t s) {
   if (nfr <= 0) return;
-  ProfScope ps(PROF_FRONTEND, s, (double)B * nfr * (2.0 * 2 * 400 * 257 + 2.0 * 257 * 2),
-               (double)B * nfr * (160 * 4 + 128 * 4));
   dim3 grid((nfr + 3) / 4, B);
-  hipLaunchKernelGGL(logmel_kernel, grid, dim3(256), 0, s, audio, a_bstride, ring_mask, n_total,
-                     t0, nfr, tab, mel, m_bstride);
+  klaunch(PROF_FRONTEND, (double)B * nfr * (2.0 * 2 * 400 * 257 + 2.0 * 257 * 2),
+          (double)B * nfr * (160 * 4 + 128 * 4), logmel_kernel, grid, dim3(256), s, audio,
+          a_bstride, ring_mask, n_total, (long long)t0, nfr, tab, mel, m_bstride);
 }
 
 // ------------------------------------------------ 8x ConvSubsampling parts

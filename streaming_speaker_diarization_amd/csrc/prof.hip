@@ -1,8 +1,8 @@
 // Per-kernel-class timing for benchmarks. While a class is being profiled,
-// every launch of that class is bracketed by a pair of HIP events recorded on
-// the launch's own stream, and the launch's algorithmic flop and byte counts
-// are accumulated (what the operation must compute and move, independent of
-// how the kernel tiles it).
+// every launch of that class carries a start/stop event pair that the
+// dispatch records around the kernel itself (hipExtLaunchKernelGGL), and the
+// launch's algorithmic flop and byte counts are accumulated (what the
+// operation must compute and move, independent of how the kernel tiles it).
 #include <vector>
 
 #include "kernels.h"
@@ -31,14 +31,10 @@ bool prof_active(int cls) {
   return p.on && p.cls == cls && p.used + 2 <= p.ev.size();
 }
 
-void prof_begin_launch(hipStream_t s) {
+void prof_next(hipEvent_t* start, hipEvent_t* stop, double flops, double bytes) {
   Prof& p = P();
-  hipEventRecord(p.ev[p.used], s);
-}
-
-void prof_end_launch(hipStream_t s, double flops, double bytes) {
-  Prof& p = P();
-  hipEventRecord(p.ev[p.used + 1], s);
+  *start = p.ev[p.used];
+  *stop = p.ev[p.used + 1];
   p.used += 2;
   p.flops += flops;
   p.bytes += bytes;
@@ -48,7 +44,7 @@ void prof_end_launch(hipStream_t s, double flops, double bytes) {
 int prof_start(int cls, int max_launches) {
   Prof& p = P();
   if (p.on || max_launches < 1) return -1;
-  for (auto e : p.ev) hipEventDestroy(e);
+  for (auto e : p.ev) (void)hipEventDestroy(e);
   p.ev.assign((size_t)2 * max_launches, nullptr);
   for (auto& e : p.ev)
     if (hipEventCreate(&e) != hipSuccess) return -4;

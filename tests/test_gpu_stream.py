@@ -28,6 +28,11 @@ def _report(name, got, ref):
     err = float(np.abs(got - ref).max())
     agree = float(np.mean((got > 0.5) == (ref > 0.5)))
     print(f"[{name}] shape {got.shape} max|dp| {err:.3e} agree {agree:.5f}", flush=True)
+    if not err <= 3e-2:  # say what the output looked like
+        bad = np.argwhere(np.abs(got - ref) > 3e-2)
+        print(f"  got range [{np.nanmin(got):.4g}, {np.nanmax(got):.4g}] nan {np.isnan(got).sum()}"
+              f" | ref range [{ref.min():.4g}, {ref.max():.4g}] | {len(bad)} entries off, first"
+              f" {bad[:4].tolist()} last {bad[-4:].tolist()}", flush=True)
     return err, agree
 
 
