@@ -49,7 +49,67 @@ def parse():
     ap.add_argument("--workload", default="low60s", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-profile", action="store_true", help="skip the profiled pass")
+    ap.add_argument("--no-graphs", action="store_true",
+                    help="launch the stream window forward kernel by kernel (no HIP graphs)")
+    ap.add_argument("--window-probe", type=int, default=0, metavar="W",
+                    help="only run the encoder over one steady-state window of W frames of the "
+                         "workload's model twice (a short program for counter collection) and exit")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB three times (the "
+                         "calibration kernel for the HBM byte counters) and exit")
     return ap.parse_args()
+
+
+# HBM traffic of the dominant kernel class from the FETCH_SIZE / WRITE_SIZE
+# counter runs, stored beside the rocprofv3 summaries together with a hash of
+# the kernel sources it was measured on; reported only while they match.
+PMC_FILE = os.path.join(ROOT, "profiles", "gemm_low60s_pmc.txt")
+PMC_SOURCES = ["gemm.hip", "kernels.h", "common.h"]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in PMC_SOURCES:
+        with open(os.path.join(ROOT, "streaming_speaker_diarization_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE), or None."""
+    try:
+        kv = dict(line.split(":", 1) for line in open(PMC_FILE) if ":" in line)
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if (kv.get("workload") != workload or kv.get("kernel_class") != kernel
+            or kv.get("kernel_sources_sha256") != kernel_source_hash()):
+        return None
+    return float(kv["hbm_bytes_per_launch"])
+
+
+def window_probe(name, wl, W):
+    import torch
+    from streaming_speaker_diarization_amd import runtime
+    m = runtime.Model(wl["arch"], wl["dtype"])
+    g = torch.Generator().manual_seed(W)
+    emb = torch.randn(wl["batch"], W, 512, generator=g).cuda()
+    for _ in range(2):
+        m.encode_window(emb)
+    torch.cuda.synchronize()
+    print(json.dumps({"window_probe": name, "frames": W, "passes": 2}), flush=True)
+
+
+def copy_probe(mib):
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_per_copy": n * 4, "copies": 3}), flush=True)
 
 
 def load_audio(name, wl):
@@ -77,14 +137,17 @@ class Runner:
         S = self.model.n_spk
         if wl["mode"] == "stream":
             self.stream = self.model.stream(wl["preset"], batch=B)
-            self.out = torch.empty(B, te, S, device="cuda")
+            # slack of one step's maximum emission: a step may be handed the
+            # tail of this buffer directly (B == 1)
+            max_emit = sf.sortformer_stream_max_emit(self.stream.handle)
+            self.out = torch.empty(B, te + max_emit, S, dtype=torch.float32, device="cuda")
             # the live schedule: samples per call, known from the library
             self.plan = None
         else:
             self.ws = self.model.workspace(
                 sf.sortformer_offline_workspace_bytes(self.model.handle, B, N))
             n_out = te if wl["arch"] == "sortformer" else 8 * te
-            self.out = torch.empty(B, n_out, S, device="cuda")
+            self.out = torch.empty(B, n_out, S, dtype=torch.float32, device="cuda")
 
     def one_pass(self):
         sf = self.sf
@@ -154,6 +217,12 @@ def cpu_baseline(name, wl, audio_np):
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
+    if args.window_probe:
+        window_probe(args.workload, WORKLOADS[args.workload], args.window_probe)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(streams shard across GPUs with no per-step exchange; see the design notes).")
@@ -164,6 +233,8 @@ def main():
     audio_np = load_audio(args.workload, wl)
     audio = torch.from_numpy(audio_np.astype(np.float32)).cuda().contiguous()
     r = Runner(args.workload, wl, audio)
+    if args.no_graphs and wl["mode"] == "stream":
+        r.sf.sortformer_stream_set_option(r.stream.handle, r.sf.SF_STREAM_OPT_GRAPHS, 0)
     for _ in range(args.warmup):
         r.one_pass()
     torch.cuda.synchronize()
@@ -199,14 +270,15 @@ def main():
         if mfma:
             ach = p["flops"] / max(p["launches"], 1) / (avg_ms / 1e3) / 1e12
             roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 3), "peak": peak,
-                    "unit": "TFLOP/s", "frac": round(ach / peak, 5), "traffic": None,
+                    "unit": "TFLOP/s", "frac": round(ach / peak, 5),
+                    "traffic": measured_traffic(args.workload, dom),
                     "launches": p["launches"], "avg_launch_us": round(1e3 * avg_ms, 3),
                     "share_of_pass": round(p["ms"] / ms_per_step, 4)}
         else:
             ach = p["bytes"] / max(p["launches"], 1) / (avg_ms / 1e3) / 1e9
             roof = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 2),
                     "peak": PEAK["hbm_gbs"], "unit": "GB/s", "frac": round(ach / PEAK["hbm_gbs"], 5),
-                    "traffic": None, "launches": p["launches"], "avg_launch_us": round(1e3 * avg_ms, 3)}
+                    "traffic": measured_traffic(args.workload, dom), "launches": p["launches"], "avg_launch_us": round(1e3 * avg_ms, 3)}
     line = {
         "metric": METRIC,
         "value": round(value, 2),

@@ -45,15 +45,15 @@ class Model:
         ws = self.workspace(sf.sortformer_offline_workspace_bytes(self.handle, B, N))
         te = (N // 160 + 7) // 8
         n_out = te if self.arch == "sortformer" else 8 * te
-        out = torch.empty(B, max(n_out, 1), self.n_spk, device=self.device)
+        out = torch.empty(B, max(n_out, 1), self.n_spk, dtype=torch.float32, device=self.device)
         got = sf.sortformer_forward_offline(self.handle, audio.contiguous(), out, ws)
         return out[:, :got]
 
     def encode_window(self, emb: torch.Tensor, n_valid: int | None = None):
         B, W, _ = emb.shape
         ws = self.workspace(sf.sortformer_encode_workspace_bytes(self.handle, B, W))
-        p = torch.empty(B, W, self.n_spk, device=self.device)
-        p10 = torch.empty(B, 8 * W, self.n_spk, device=self.device) \
+        p = torch.empty(B, W, self.n_spk, dtype=torch.float32, device=self.device)
+        p10 = torch.empty(B, 8 * W, self.n_spk, dtype=torch.float32, device=self.device) \
             if self.arch == "nemotron" else None
         sf.sortformer_encode_window(self.handle, emb.contiguous(), W if n_valid is None else n_valid,
                                     p, p10, ws)
@@ -64,8 +64,8 @@ class Model:
         T = N // 160
         te = (T + 7) // 8
         ws = self.workspace(sf.sortformer_pre_encode_workspace_bytes(self.handle, B, N))
-        mel = torch.empty(B, max(T, 1), 128, device=self.device)
-        emb = torch.empty(B, max(te, 1), 512, device=self.device)
+        mel = torch.empty(B, max(T, 1), 128, dtype=torch.float32, device=self.device)
+        emb = torch.empty(B, max(te, 1), 512, dtype=torch.float32, device=self.device)
         sf.sortformer_pre_encode(self.handle, audio.contiguous(), mel, emb, ws)
         return mel[:, :T], emb[:, :te]
 
@@ -85,7 +85,7 @@ class Stream:
                          model.device)
         self.handle = sf.sortformer_stream_create(model.handle, scfg, batch, self.state)
         self.out = torch.empty(batch, sf.sortformer_stream_max_emit(self.handle), model.n_spk,
-                               device=model.device)
+                               dtype=torch.float32, device=model.device)
 
     def __del__(self):
         h = getattr(self, "handle", None)

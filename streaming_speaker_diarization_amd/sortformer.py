@@ -115,8 +115,32 @@ def _check(st, what):
         raise SortformerError(st, what)
 
 
-def _ptr(t):
-    return None if t is None else C.c_void_p(t.data_ptr())
+def _ptr(t, min_numel=0):
+    """Device address of a contiguous float32 tensor on the GPU (None passes
+    through); raises before anything is launched when the tensor is on the
+    host, strided, of another dtype or shorter than min_numel elements."""
+    import torch
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise TypeError("expected a tensor in device memory")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    if t.dtype != torch.float32:
+        raise TypeError(f"expected a float32 tensor, got {t.dtype}")
+    if t.numel() < min_numel:
+        raise ValueError(f"buffer holds {t.numel()} elements, {min_numel} needed")
+    return C.c_void_p(t.data_ptr())
+
+
+def _buf(t):
+    """(address, size in bytes) of a contiguous device byte buffer (workspace,
+    stream state or weight arena) of any dtype."""
+    if not t.is_cuda:
+        raise TypeError("expected a buffer in device memory")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous buffer")
+    return C.c_void_p(t.data_ptr()), t.numel() * t.element_size()
 
 
 def _stream(s):
@@ -150,8 +174,8 @@ def sortformer_weight_bytes(cfg: sf_model_config) -> int:
 
 def sortformer_init(cfg, seed, d_weights, stream=None):
     h = C.c_void_p()
-    _check(load().sortformer_init(C.byref(cfg), seed, _ptr(d_weights), d_weights.numel() *
-                                  d_weights.element_size(), _stream(stream), C.byref(h)), "init")
+    _check(load().sortformer_init(C.byref(cfg), seed, *_buf(d_weights), _stream(stream),
+                                  C.byref(h)), "init")
     return h
 
 
@@ -204,9 +228,14 @@ def sortformer_offline_workspace_bytes(h, batch, n_samples) -> int:
 def sortformer_forward_offline(h, d_audio, d_probs, d_ws, stream=None) -> int:
     B, N = d_audio.shape
     n_out = C.c_int64()
-    _check(load().sortformer_forward_offline(h, _ptr(d_audio), B, N, _ptr(d_probs),
-                                             C.byref(n_out), _ptr(d_ws), d_ws.numel(),
-                                             _stream(stream)), "forward_offline")
+    cfg = sf_model_config()
+    _check(load().sortformer_get_config(h, C.byref(cfg)), "get_config")
+    te = (N // 160 + 7) // 8
+    rows = te if cfg.arch == SF_ARCH_SORTFORMER else 8 * te
+    _check(load().sortformer_forward_offline(h, _ptr(d_audio), B, N,
+                                             _ptr(d_probs, B * rows * cfg.n_spk),
+                                             C.byref(n_out), *_buf(d_ws), _stream(stream)),
+           "forward_offline")
     return n_out.value
 
 
@@ -220,15 +249,18 @@ def sortformer_stream_workspace_bytes(h, scfg, batch) -> int:
 
 def sortformer_stream_create(h, scfg, batch, d_state, stream=None):
     st = C.c_void_p()
-    _check(load().sortformer_stream_create(h, C.byref(scfg), batch, _ptr(d_state),
-                                           d_state.numel(), _stream(stream), C.byref(st)),
+    cfg = sf_model_config()
+    _check(load().sortformer_get_config(h, C.byref(cfg)), "get_config")
+    _check(load().sortformer_stream_create(h, C.byref(scfg), batch, *_buf(d_state),
+                                           _stream(stream), C.byref(st)),
            "stream_create")
-    _BATCH[st.value] = batch
+    _STREAMS[st.value] = (batch, cfg.n_spk)
     return st
 
 
 def sortformer_stream_destroy(st):
     load().sortformer_stream_destroy(st)
+    _STREAMS.pop(getattr(st, "value", st), None)
 
 
 def sortformer_stream_set_option(st, option, value):
@@ -249,8 +281,10 @@ def sortformer_stream_max_emit(st) -> int:
 
 def sortformer_stream_step(st, d_audio_new, n_new, is_last, d_probs_out, d_ws, stream=None) -> int:
     n = C.c_int32()
-    _check(load().sortformer_stream_step(st, _ptr(d_audio_new), n_new, int(is_last),
-                                         _ptr(d_probs_out), C.byref(n), _ptr(d_ws), d_ws.numel(),
+    B, S = _STREAMS[st.value]
+    _check(load().sortformer_stream_step(st, _ptr(d_audio_new, B * n_new), n_new, int(is_last),
+                                         _ptr(d_probs_out, B * sortformer_stream_max_emit(st) * S),
+                                         C.byref(n), *_buf(d_ws),
                                          _stream(stream)), "stream_step")
     return n.value
 
@@ -296,16 +330,16 @@ def sortformer_stream_import(st, cache_len, fifo_len, lookahead_len, emb, probs,
            "stream_import")
 
 
-_BATCH = {}
+_STREAMS = {}  # stream handle -> (batch, speakers)
 
 
 def _stream_batch(st):
-    return _BATCH[st.value]
+    return _STREAMS[st.value][0]
 
 
 def sortformer_stream_update(st, d_window_probs, n_chunk, d_ws, stream=None):
-    _check(load().sortformer_stream_update(st, _ptr(d_window_probs), n_chunk, _ptr(d_ws),
-                                           d_ws.numel(), _stream(stream)), "stream_update")
+    _check(load().sortformer_stream_update(st, _ptr(d_window_probs), n_chunk, *_buf(d_ws),
+                                           _stream(stream)), "stream_update")
 
 
 def sortformer_encode_workspace_bytes(h, batch, window) -> int:
@@ -313,10 +347,15 @@ def sortformer_encode_workspace_bytes(h, batch, window) -> int:
 
 
 def sortformer_encode_window(h, d_emb, n_valid, d_probs, d_probs10, d_ws, stream=None):
-    B, W, _ = d_emb.shape
-    _check(load().sortformer_encode_window(h, _ptr(d_emb), B, W, n_valid, _ptr(d_probs),
-                                           _ptr(d_probs10), _ptr(d_ws), d_ws.numel(),
-                                           _stream(stream)), "encode_window")
+    B, W, D = d_emb.shape
+    cfg = sf_model_config()
+    _check(load().sortformer_get_config(h, C.byref(cfg)), "get_config")
+    if D != 512:
+        raise ValueError("embeddings must have 512 features")
+    _check(load().sortformer_encode_window(h, _ptr(d_emb), B, W, n_valid,
+                                           _ptr(d_probs, B * W * cfg.n_spk),
+                                           _ptr(d_probs10, 8 * B * W * cfg.n_spk),
+                                           *_buf(d_ws), _stream(stream)), "encode_window")
 
 
 def sortformer_pre_encode_workspace_bytes(h, batch, n_samples) -> int:
@@ -325,8 +364,10 @@ def sortformer_pre_encode_workspace_bytes(h, batch, n_samples) -> int:
 
 def sortformer_pre_encode(h, d_audio, d_mel, d_emb, d_ws, stream=None):
     B, N = d_audio.shape
-    _check(load().sortformer_pre_encode(h, _ptr(d_audio), B, N, _ptr(d_mel), _ptr(d_emb),
-                                        _ptr(d_ws), d_ws.numel(), _stream(stream)), "pre_encode")
+    T = N // 160
+    _check(load().sortformer_pre_encode(h, _ptr(d_audio), B, N, _ptr(d_mel, B * T * 128),
+                                        _ptr(d_emb, B * ((T + 7) // 8) * 512), *_buf(d_ws),
+                                        _stream(stream)), "pre_encode")
 
 
 def sortformer_profile_begin(kind: str, max_launches: int = 20000):

@@ -102,3 +102,13 @@ def test_no_cpu_fallback_in_product_path():
         if f.endswith(".py"):
             txt = open(os.path.join(pkg, f)).read()
             assert "import oracle" not in txt and "from oracle" not in txt, f
+
+
+def test_binding_rejects_host_strided_or_mistyped_tensors():
+    import torch
+    from streaming_speaker_diarization_amd import sortformer
+    with pytest.raises(TypeError):
+        sortformer._ptr(torch.zeros(4, dtype=torch.float32))  # host memory
+    with pytest.raises(TypeError):
+        sortformer._buf(torch.zeros(4, dtype=torch.uint8))
+    assert sortformer._ptr(None) is None

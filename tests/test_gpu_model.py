@@ -151,3 +151,24 @@ def test_offline_fp32_batched_matches_single(sf32):
     both = sf32.offline(_cuda(a)).cpu().numpy()
     one = sf32.offline(_cuda(a[1:])).cpu().numpy()
     assert np.array_equal(both[1], one[0])   # same kernels, same order: bit-identical
+
+
+def test_binding_checks_and_default_dtype_independence(sf32):
+    """The runtime allocates float32 whatever torch's default dtype is, and the
+    binding refuses mistyped or short buffers before launching anything."""
+    from streaming_speaker_diarization_amd import sortformer as sf
+    audio = _cuda(meeting_audio(3.0, 2, 11))[None]
+    ref = sf32.offline(audio).cpu()
+    old = torch.get_default_dtype()
+    torch.set_default_dtype(torch.float64)
+    try:
+        got = sf32.offline(audio).cpu()
+    finally:
+        torch.set_default_dtype(old)
+    assert got.dtype == torch.float32 and torch.equal(got, ref)
+    ws = sf32.workspace(sf.sortformer_offline_workspace_bytes(sf32.handle, 1, audio.shape[1]))
+    with pytest.raises(TypeError):
+        sf.sortformer_forward_offline(sf32.handle, audio.double(), torch.empty(1, 38, 4).cuda(), ws)
+    with pytest.raises(ValueError):
+        sf.sortformer_forward_offline(sf32.handle, audio,
+                                      torch.empty(1, 10, 4, dtype=torch.float32).cuda(), ws)

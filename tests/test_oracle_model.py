@@ -14,7 +14,6 @@ from oracle import sortformer as SF
 from oracle import run, streaming
 
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_facts.json")))
-torch.set_default_dtype(torch.float64)
 
 
 def _t(x):
@@ -273,7 +272,8 @@ def test_nemotron_layer_vs_torch(nm_weights_full):
 
     q, k, v = heads("q"), heads("k"), heads("v")
     # rotary applied as complex multiplication (an independent formulation)
-    ang = torch.arange(W)[:, None] * 10000.0 ** (-torch.arange(32) / 32)
+    f64 = torch.float64  # every tensor here is fp64 (no process-wide default is set)
+    ang = torch.arange(W, dtype=f64)[:, None] * 10000.0 ** (-torch.arange(32, dtype=f64) / 32)
     rot = torch.polar(torch.ones_like(ang), ang)
 
     def rope_c(t):
