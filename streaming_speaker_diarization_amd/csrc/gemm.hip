@@ -43,70 +43,150 @@ __device__ __forceinline__ void qkv_store(const GemmArgs& g, int m, int n, float
   }
 }
 
-// Epilogue over one wave's TMxTN grid of 16x16 accumulators. Lane l holds
-// rows 4*(l/16)+r, column l%16 of each tile. GLU: the weight rows were
-// interleaved in blocks of 16 (value, gate), so tiles 2p and 2p+1 hold the
-// value and gate halves of the same 16 output columns.
-template <int EPI, typename OutT, int TM, int TN>
-__device__ __forceinline__ void epilogue(const GemmArgs& g, f32x4 (&acc)[TM][TN], int mb, int nb,
-                                         int lane, int split) {
+template <int EPI>
+__device__ __forceinline__ float activate(float v) {
+  if constexpr (EPI == EPI_SWISH) v = swishf_(v);
+  if constexpr (EPI == EPI_RELU) v = fmaxf(v, 0.f);
+  if constexpr (EPI == EPI_GELU) v = geluf_(v);
+  return v;
+}
+
+// Output columns of a BN-wide tile (GLU halves them).
+template <int EPI, int BN> struct TileCols { static constexpr int C = EPI == EPI_GLU ? BN / 2 : BN; };
+
+// LDS bytes the staged epilogue needs for a BM x BN tile (fp32, padded rows).
+template <int EPI, int BM, int BN>
+constexpr int stage_bytes() { return BM * (TileCols<EPI, BN>::C + 4) * 4; }
+
+// Epilogue, step 1: every wave writes its TMxTN grid of 16x16 accumulators
+// (lane l: rows 4*(l/16)+r, column l%16 of each tile) with bias and
+// activation applied into an fp32 tile in LDS. GLU: the weight rows were
+// interleaved in blocks of 16 (value, gate), so accumulator tiles 2p and 2p+1
+// hold the value and gate halves of the same 16 output columns.
+template <int EPI, int BN, int TM, int TN>
+__device__ __forceinline__ void stage_tile(const GemmArgs& g, const f32x4 (&acc)[TM][TN],
+                                           float* cs, int n0, int wr, int wc, int lane) {
+  constexpr int LDC = TileCols<EPI, BN>::C + 4;
+  const int c16 = lane & 15, g4 = 4 * (lane >> 4);
   if constexpr (EPI == EPI_GLU) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int p = 0; p < TN / 2; ++p) {
+      const int na = n0 + wc + 32 * p + c16;
+      const float ba = g.bias ? g.bias[na] : 0.f, bg = g.bias ? g.bias[na + 16] : 0.f;
+      const int oc = (wc + 32 * p) / 2 + c16;
 #pragma unroll
-      for (int p = 0; p < TN / 2; ++p) {
-        const int nn = nb + 32 * p;
-        const int na = nn + (lane & 15);
-        const float ba = g.bias ? g.bias[na] : 0.f, bg = g.bias ? g.bias[na + 16] : 0.f;
-        const int oc = nn / 2 + (lane & 15);
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = mb + 16 * i + 4 * (lane >> 4) + r;
-          if (m < g.M) {
-            OutT* out = static_cast<OutT*>(g.out);
-            out[(size_t)m * g.ldo + oc] =
-                from_f<OutT>((acc[i][2 * p][r] + ba) * sigmoidf_(acc[i][2 * p + 1][r] + bg));
-          }
-        }
-      }
+        for (int r = 0; r < 4; ++r)
+          cs[(wr + 16 * i + g4 + r) * LDC + oc] =
+              (acc[i][2 * p][r] + ba) * sigmoidf_(acc[i][2 * p + 1][r] + bg);
+    }
   } else {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int j = 0; j < TN; ++j) {
+      const int c = wc + 16 * j + c16;
+      const float bn = (EPI != EPI_PARTIAL && g.bias) ? g.bias[n0 + c] : 0.f;
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int n = nb + 16 * j + (lane & 15);
-        const float bn = (EPI != EPI_PARTIAL && g.bias) ? g.bias[n] : 0.f;
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = mb + 16 * i + 4 * (lane >> 4) + r;
-          if (m >= g.M) continue;
-          if constexpr (EPI == EPI_PARTIAL) {
-            float* part = static_cast<float*>(g.out);
-            part[((size_t)split * g.M + m) * g.N + n] = acc[i][j][r];
-          } else if constexpr (EPI == EPI_QKV) {
-            if (n < g.vcol || sizeof(OutT) != 2) {
-              qkv_store<OutT>(g, m, n, acc[i][j][r] + bn);
-            } else if (r == 0) {
-              // rows m..m+3 of one V column are 4 consecutive keys of V^T
-              const int nn = n - g.vcol, hh = nn / g.vhd, d = nn % g.vhd;
-              const int bb = m / g.vrows, w0 = m % g.vrows, H = (g.N - g.vcol) / g.vhd;
-              if (m + 3 < g.M && w0 + 3 < g.vrows && (w0 & 3) == 0) {
-                uint2 pk;
-                pk.x = (uint32_t)f2bf(acc[i][j][0] + bn) | ((uint32_t)f2bf(acc[i][j][1] + bn) << 16);
-                pk.y = (uint32_t)f2bf(acc[i][j][2] + bn) | ((uint32_t)f2bf(acc[i][j][3] + bn) << 16);
-                *reinterpret_cast<uint2*>(static_cast<bf16_t*>(g.vt) +
-                                          ((size_t)(bb * H + hh) * g.vhd + d) * g.vpitch + w0) = pk;
-              } else {
+        for (int r = 0; r < 4; ++r)
+          cs[(wr + 16 * i + g4 + r) * LDC + c] = activate<EPI>(acc[i][j][r] + bn);
+    }
+  }
+}
+
+template <typename OutT> struct OutVec;
+template <> struct OutVec<float> {
+  static constexpr int E = 4;  // elements per 16-byte store
+  __device__ static void put(float* p, const float* v) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+};
+template <> struct OutVec<bf16_t> {
+  static constexpr int E = 8;
+  __device__ static void put(bf16_t* p, const float* v) {
+    uint4 u;
+    u.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+    u.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+    u.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
+    u.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
+    *reinterpret_cast<uint4*>(p) = u;
+  }
+};
+
+__device__ __forceinline__ bool aligned16(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15) == 0;
+}
+
+// Epilogue, step 2 (after a barrier): the workgroup stores the staged tile
+// with 16-byte row-contiguous writes (V columns of EPI_QKV: contiguous along
+// the keys of V^T). Rows past M are skipped; a chunk that is misaligned or
+// crosses a stream boundary of V^T falls back to element stores.
+template <int EPI, typename OutT, int BM, int BN>
+__device__ __forceinline__ void store_tile(const GemmArgs& g, const float* cs, int m0, int n0,
+                                           int split, int tid) {
+  constexpr int C = TileCols<EPI, BN>::C;
+  constexpr int LDC = C + 4;
+  if constexpr (EPI == EPI_PARTIAL) {
+    float* part = static_cast<float*>(g.out);
+    for (int q = tid; q < BM * C / 4; q += 256) {
+      const int r = q / (C / 4), c = (q % (C / 4)) * 4, m = m0 + r;
+      if (m < g.M)
+        *reinterpret_cast<float4*>(part + ((size_t)split * g.M + m) * g.N + n0 + c) =
+            *reinterpret_cast<const float4*>(cs + r * LDC + c);
+    }
+    return;
+  }
+  constexpr int E = OutVec<OutT>::E;
+  if constexpr (EPI == EPI_QKV) {
+    if (n0 >= g.vcol) {  // V block: column c of the tile is one (head, dim) row of V^T
+      OutT* vt = static_cast<OutT*>(g.vt);
+      const int H = (g.N - g.vcol) / g.vhd;
+      for (int q = tid; q < BM / E * C; q += 256) {
+        const int c = q / (BM / E), r = (q % (BM / E)) * E, m = m0 + r;
+        if (m >= g.M) continue;
+        const int nn = n0 + c - g.vcol, hh = nn / g.vhd, d = nn % g.vhd;
+        const int bb = m / g.vrows, w = m % g.vrows;
+        OutT* dst = vt + ((size_t)(bb * H + hh) * g.vhd + d) * g.vpitch + w;
+        float v[E];
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                  if (m + q < g.M) qkv_store<OutT>(g, m + q, n, acc[i][j][q] + bn);
-              }
-            }
-          } else {
-            epi_store<EPI, OutT>(g, m, n, acc[i][j][r] + bn);
+        for (int e = 0; e < E; ++e) v[e] = cs[(r + e) * LDC + c];
+        if (m + E <= g.M && w + E <= g.vrows && aligned16(dst)) {
+          OutVec<OutT>::put(dst, v);
+        } else {
+          for (int e = 0; e < E && m + e < g.M; ++e) {
+            const int b2 = (m + e) / g.vrows, w2 = (m + e) % g.vrows;
+            vt[((size_t)(b2 * H + hh) * g.vhd + d) * g.vpitch + w2] = from_f<OutT>(v[e]);
           }
         }
       }
+      return;
+    }
+  }
+  OutT* out = static_cast<OutT*>(g.out);
+  for (int q = tid; q < BM * C / E; q += 256) {
+    const int r = q / (C / E), c = (q % (C / E)) * E, m = m0 + r;
+    if (m >= g.M) continue;
+    const size_t row = g.rpb ? (size_t)(m / g.rpb) * g.bstride + (size_t)(m % g.rpb) * g.ldo
+                             : (size_t)m * g.ldo;
+    const int oc = (EPI == EPI_GLU ? n0 / 2 : n0) + c;
+    float v[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e] = cs[r * LDC + c + e];
+    OutT* dst = out + row + oc;
+    if (aligned16(dst)) {
+      OutVec<OutT>::put(dst, v);
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) dst[e] = from_f<OutT>(v[e]);
+    }
+    if constexpr (EPI == EPI_STORE) {
+      if (g.resid) {
+        float* rd = g.resid + (size_t)m * g.ldr + oc;
+#pragma unroll
+        for (int e = 0; e < E; ++e) rd[e] = v[e];
+      }
+    }
   }
 }
 
@@ -127,8 +207,10 @@ __global__ __launch_bounds__(256) void gemm_slice_kernel(GemmArgs g) {
   constexpr int NCH = 64 * CPR / 256;        // 16-byte chunks per thread per operand
   static_assert(64 * CPR % 256 == 0, "slice width");
   using M_ = MF<T>;
-  __shared__ __align__(16) T As[64 * LD];
-  __shared__ __align__(16) T Bs[64 * LD];
+  constexpr int AB = 2 * 64 * LD * (int)sizeof(T), ST = stage_bytes<EPI, 64, 64>();
+  __shared__ __align__(16) char smem[AB > ST ? AB : ST];
+  T* As = reinterpret_cast<T*>(smem);
+  T* Bs = As + 64 * LD;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int n0 = blockIdx.x * 64, m0 = blockIdx.y * 64, split = blockIdx.z;
@@ -171,7 +253,11 @@ __global__ __launch_bounds__(256) void gemm_slice_kernel(GemmArgs g) {
     acc[1][0] = M_::mma(a1, b0, acc[1][0]);
     acc[1][1] = M_::mma(a1, b1, acc[1][1]);
   }
-  epilogue<EPI, OutT, 2, 2>(g, acc, m0 + wm * 32, n0 + wn * 32, lane, split);
+  __syncthreads();  // every wave is done with As/Bs: the tile is staged over them
+  float* cs = reinterpret_cast<float*>(smem);
+  stage_tile<EPI, 64, 2, 2>(g, acc, cs, n0, wm * 32, wn * 32, lane);
+  __syncthreads();
+  store_tile<EPI, OutT, 64, 64>(g, cs, m0, n0, split, tid);
 }
 
 // ------------------------------------------------------------- loop kernel
@@ -186,8 +272,10 @@ __global__ __launch_bounds__(256) void gemm_loop_kernel(GemmArgs g, int ks) {
   constexpr int A_IT = BM * CPR / 256;
   constexpr int B_IT = BN * CPR / 256;
   using M_ = MF<T>;
-  __shared__ __align__(16) T As[2][BM * LDK];
-  __shared__ __align__(16) T Bs[2][BN * LDK];
+  constexpr int AB = 2 * (BM + BN) * LDK * (int)sizeof(T), ST = stage_bytes<EPI, BM, BN>();
+  __shared__ __align__(16) char smem[AB > ST ? AB : ST];
+  T (*As)[BM * LDK] = reinterpret_cast<T (*)[BM * LDK]>(smem);
+  T (*Bs)[BN * LDK] = reinterpret_cast<T (*)[BN * LDK]>(smem + 2 * BM * LDK * sizeof(T));
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -256,7 +344,11 @@ __global__ __launch_bounds__(256) void gemm_loop_kernel(GemmArgs g, int ks) {
     if (kt + 1 < nk) stash(cur ^ 1);
     __syncthreads();
   }
-  epilogue<EPI, OutT, TM, TN>(g, acc, m0 + wm * WM, n0 + wn * WN, lane, split);
+  __syncthreads();
+  float* cs = reinterpret_cast<float*>(smem);
+  stage_tile<EPI, BN, TM, TN>(g, acc, cs, n0, wm * WM, wn * WN, lane);
+  __syncthreads();
+  store_tile<EPI, OutT, BM, BN>(g, cs, m0, n0, split, tid);
 }
 
 // ------------------------------------------------- split-K reduce + epilogue
