@@ -62,23 +62,6 @@ template <> struct Frag<float> {
   __device__ static type zero_if(const type& f, unsigned live_mask) { return live_mask & 1u ? f : 0.f; }
 };
 
-// Reductions over the 16 lanes of one MFMA row group with DPP (no LDS):
-// quad swaps (xor 1, xor 2), then rotations by 4 and 8 within the row.
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false)));
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false)));
-  return v;
-}
-__device__ __forceinline__ float row16_sum(float v) {
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
-  return v;
-}
-
 // LDS hand-off between lanes of one wave (the producer and consumer are the
 // same wave, so waiting for its LDS operations is enough).
 __device__ __forceinline__ void wave_lds_sync() {
@@ -86,15 +69,15 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-// One workgroup = 16 query rows of one (stream, head); its 4 waves take the
+// One workgroup = 16 query rows of one (stream, head); its NW waves take the
 // key tiles (64 frames) round-robin and merge their partial softmax states at
 // the end. MFMA B operands are read straight from global memory (L2):
 //  K rows   [key][dim]          -> scores  S = Q K^T
 //  p band   [delta][dim]        -> G = (q+v) p(delta)^T  (relative position)
 //  V^T rows [dim][key]          -> O += P V
 // so the only LDS traffic is the score shift (G) and the re-layout of P.
-template <typename T, int HD, int MODE>
-__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
+template <typename T, int HD, int MODE, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   using M_ = MF<T>;
   using F = Frag<T>;
   typedef typename F::type frag_t;
@@ -108,10 +91,10 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   constexpr bool REL = MODE == ATT_RELPOS;
   constexpr bool ROPE = MODE == ATT_ROPE;
   static_assert(!ROPE || HD == 64, "rotary layers use 64-dim heads");
-  __shared__ float Gs[REL ? 4 * 16 * 81 : 1];
-  __shared__ __align__(16) T Ps[4 * 16 * LDP];
-  __shared__ float Ms[4][16], Ls[4][16];
-  __shared__ float Os[4][16][HDP + 1];
+  __shared__ float Gs[REL ? NW * 16 * 81 : 1];
+  __shared__ __align__(16) T Ps[NW * 16 * LDP];
+  __shared__ float Ms[NW][16], Ls[NW][16];
+  __shared__ float Os[NW][16][HDP + 1];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c16 = lane & 15;
   const int iq0 = blockIdx.x * 16, h = blockIdx.y, b = blockIdx.z;
@@ -219,7 +202,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 
   const int ntile = (a.n_valid + 63) / 64;
   if (w < ntile) load_kb(w * 64);
-  for (int kt = w; kt < ntile; kt += 4) {
+  for (int kt = w; kt < ntile; kt += NW) {
     const int j0 = kt * 64;
     load_v(j0);
     // the loads are unconditional: zero what lies outside the head / window
@@ -285,7 +268,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         for (int r = 0; r < 4; ++r)
           S[nt][r] += G[(4 * g + r) * 81 + (4 * g + r) - (16 * nt + c16) + 63];
     }
-    if (kt + 4 < ntile) load_kb(j0 + 256);  // next tile of this wave, in flight now
+    if (kt + NW < ntile) load_kb(j0 + 64 * NW);  // next tile of this wave, in flight now
 
     // ---- online softmax (log2 domain)
     float mx[4];
@@ -342,14 +325,14 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     for (int r = 0; r < 4; ++r) Os[w][4 * g + r][16 * dt + c16] = O[dt][r];
   __syncthreads();
   T* ctx = static_cast<T*>(a.ctx);
-  for (int o = tid; o < 16 * HD; o += 256) {
+  for (int o = tid; o < 16 * HD; o += NW * 64) {
     const int r = o / HD, d = o % HD, i = iq0 + r;
     float mx = Ms[0][r];
 #pragma unroll
-    for (int v = 1; v < 4; ++v) mx = fmaxf(mx, Ms[v][r]);
+    for (int v = 1; v < NW; ++v) mx = fmaxf(mx, Ms[v][r]);
     float l = 0.f, acc = 0.f;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
+    for (int v = 0; v < NW; ++v) {
       const float f = exp2f(Ms[v][r] - mx);  // waves without tiles: exp2(-inf) = 0
       l += Ls[v][r] * f;
       acc += Os[v][r][d] * f;
@@ -358,17 +341,26 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   }
 }
 
+template <typename T, int NW>
+static void launch_attn_nw(const AttnArgs& a, int mode, int hd, hipStream_t s, double fl, double by) {
+  dim3 grid((a.W + 15) / 16, a.H, a.B), block(NW * 64);
+  if (mode == ATT_RELPOS && hd == 64)
+    klaunch(PROF_ATTN, fl, by, attn_kernel<T, 64, ATT_RELPOS, NW>, grid, block, s, a);
+  else if (mode == ATT_ROPE && hd == 64)
+    klaunch(PROF_ATTN, fl, by, attn_kernel<T, 64, ATT_ROPE, NW>, grid, block, s, a);
+  else if (mode == ATT_PLAIN && hd == 24)
+    klaunch(PROF_ATTN, fl, by, attn_kernel<T, 24, ATT_PLAIN, NW>, grid, block, s, a);
+  else if (mode == ATT_PLAIN && hd == 64)
+    klaunch(PROF_ATTN, fl, by, attn_kernel<T, 64, ATT_PLAIN, NW>, grid, block, s, a);
+}
+
+// Four waves per workgroup: eight gave no gain for one stream and cost a
+// third more time for 64 streams (twice the LDS, fewer workgroups per CU).
+// The split of key tiles over waves is fixed, so a stream's result does not
+// depend on how many streams share the launch.
 template <typename T>
 static void launch_attn(const AttnArgs& a, int mode, int hd, hipStream_t s, double fl, double by) {
-  dim3 grid((a.W + 15) / 16, a.H, a.B);  // 4 waves per 16 query rows
-  if (mode == ATT_RELPOS && hd == 64)
-    klaunch(PROF_ATTN, fl, by, attn_kernel<T, 64, ATT_RELPOS>, grid, dim3(256), s, a);
-  else if (mode == ATT_ROPE && hd == 64)
-    klaunch(PROF_ATTN, fl, by, attn_kernel<T, 64, ATT_ROPE>, grid, dim3(256), s, a);
-  else if (mode == ATT_PLAIN && hd == 24)
-    klaunch(PROF_ATTN, fl, by, attn_kernel<T, 24, ATT_PLAIN>, grid, dim3(256), s, a);
-  else if (mode == ATT_PLAIN && hd == 64)
-    klaunch(PROF_ATTN, fl, by, attn_kernel<T, 64, ATT_PLAIN>, grid, dim3(256), s, a);
+  launch_attn_nw<T, 4>(a, mode, hd, s, fl, by);
 }
 
 void attention(const AttnArgs& a, int mode, int head_dim, bool bf16, hipStream_t s) {

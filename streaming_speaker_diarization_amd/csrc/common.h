@@ -56,28 +56,40 @@ template <> struct MF<bf16_t> {
   }
 };
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+// Reductions over the 16 lanes of each row (lanes 16r..16r+15) with DPP, no
+// LDS: quad swaps (xor 1, xor 2), then rotations by 4 and 8 within the row;
+// every lane ends with its row's result.
+#define SF_DPP(v, ctrl) \
+  __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, 0xF, 0xF, false))
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, SF_DPP(v, 0xB1));
+  v = fmaxf(v, SF_DPP(v, 0x4E));
+  v = fmaxf(v, SF_DPP(v, 0x124));
+  v = fmaxf(v, SF_DPP(v, 0x128));
   return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += SF_DPP(v, 0xB1);
+  v += SF_DPP(v, 0x4E);
+  v += SF_DPP(v, 0x124);
+  v += SF_DPP(v, 0x128);
+  return v;
+}
+#undef SF_DPP
+
+// Whole-wave reductions (all 64 lanes active): the four row results are read
+// back as scalars, so the result is wave-uniform.
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = row16_max(v);
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
-// reductions over the 16 lanes that share l/16 (one MFMA D row group)
-__device__ __forceinline__ float group16_sum(float v) {
-#pragma unroll
-  for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-__device__ __forceinline__ float group16_max(float v) {
-#pragma unroll
-  for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
 __device__ __forceinline__ float swishf_(float x) { return x / (1.0f + __expf(-x)); }
 __device__ __forceinline__ float geluf_(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }

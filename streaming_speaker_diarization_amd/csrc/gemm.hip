@@ -199,65 +199,77 @@ template <> struct SliceCfg<float> { static constexpr int KMAX = 256; };
 // fixed number of unconditional 16-byte loads: rows past M read a clamped
 // (valid) row and are zeroed by a select afterwards, so no load sits behind a
 // branch and all of them are in flight together.
-template <typename T, typename OutT, int EPI, int KS>
+template <typename T, typename OutT, int EPI, int KS, int BM>
 __global__ __launch_bounds__(256) void gemm_slice_kernel(GemmArgs g) {
   constexpr int VEC = 16 / (int)sizeof(T);
   constexpr int LD = KS + VEC;
   constexpr int CPR = KS / VEC;
-  constexpr int NCH = 64 * CPR / 256;        // 16-byte chunks per thread per operand
-  static_assert(64 * CPR % 256 == 0, "slice width");
+  constexpr int NCA = BM * CPR / 256;        // 16-byte chunks per thread: A
+  constexpr int NCB = 64 * CPR / 256;        // and W
+  constexpr int TM = BM / 32;                // 16-row MFMA tiles per wave (waves 2 x 2)
+  static_assert(BM * CPR % 256 == 0 && 64 * CPR % 256 == 0, "slice width");
   using M_ = MF<T>;
-  constexpr int AB = 2 * 64 * LD * (int)sizeof(T), ST = stage_bytes<EPI, 64, 64>();
+  constexpr int AB = (BM + 64) * LD * (int)sizeof(T), ST = stage_bytes<EPI, BM, 64>();
   __shared__ __align__(16) char smem[AB > ST ? AB : ST];
   T* As = reinterpret_cast<T*>(smem);
-  T* Bs = As + 64 * LD;
+  T* Bs = As + BM * LD;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int n0 = blockIdx.x * 64, m0 = blockIdx.y * 64, split = blockIdx.z;
+  const int n0 = blockIdx.x * 64, m0 = blockIdx.y * BM, split = blockIdx.z;
   const int k0 = split * KS;
   const T* A = static_cast<const T*>(g.A);
   const T* Wt = static_cast<const T*>(g.W);
 
-  vec16 ra[NCH], rb[NCH];
+  vec16 ra[NCA], rb[NCB];
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) {
+  for (int i = 0; i < NCA; ++i) {
     const int c = tid + 256 * i, r = c / CPR, kc = (c % CPR) * VEC;
-    const int m = min(m0 + r, g.M - 1);
-    ra[i] = *reinterpret_cast<const vec16*>(A + (size_t)m * g.lda + k0 + kc);
+    ra[i] = *reinterpret_cast<const vec16*>(A + (size_t)min(m0 + r, g.M - 1) * g.lda + k0 + kc);
+  }
+#pragma unroll
+  for (int i = 0; i < NCB; ++i) {
+    const int c = tid + 256 * i, r = c / CPR, kc = (c % CPR) * VEC;
     rb[i] = *reinterpret_cast<const vec16*>(Wt + (size_t)(n0 + r) * g.ldw + k0 + kc);
   }
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) {
+  for (int i = 0; i < NCA; ++i) {
     const int c = tid + 256 * i, r = c / CPR, kc = (c % CPR) * VEC;
     const bool live = m0 + r < g.M;
 #pragma unroll
     for (int q = 0; q < 4; ++q) ra[i].w[q] = live ? ra[i].w[q] : 0u;
     *reinterpret_cast<vec16*>(&As[r * LD + kc]) = ra[i];
+  }
+#pragma unroll
+  for (int i = 0; i < NCB; ++i) {
+    const int c = tid + 256 * i, r = c / CPR, kc = (c % CPR) * VEC;
     *reinterpret_cast<vec16*>(&Bs[r * LD + kc]) = rb[i];
   }
   __syncthreads();
 
-  f32x4 acc[2][2];
+  f32x4 acc[TM][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const T* ap = &As[(wm * 32 + (lane & 15)) * LD];
+  const T* ap = &As[(wm * (BM / 2) + (lane & 15)) * LD];
   const T* bp = &Bs[(wn * 32 + (lane & 15)) * LD];
 #pragma unroll 4
   for (int k = 0; k < KS; k += M_::KI) {
-    typename M_::frag a0 = M_::ld(ap + k, lane), a1 = M_::ld(ap + 16 * LD + k, lane);
+    typename M_::frag af[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[i] = M_::ld(ap + 16 * i * LD + k, lane);
     typename M_::frag b0 = M_::ld(bp + k, lane), b1 = M_::ld(bp + 16 * LD + k, lane);
-    acc[0][0] = M_::mma(a0, b0, acc[0][0]);
-    acc[0][1] = M_::mma(a0, b1, acc[0][1]);
-    acc[1][0] = M_::mma(a1, b0, acc[1][0]);
-    acc[1][1] = M_::mma(a1, b1, acc[1][1]);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      acc[i][0] = M_::mma(af[i], b0, acc[i][0]);
+      acc[i][1] = M_::mma(af[i], b1, acc[i][1]);
+    }
   }
   __syncthreads();  // every wave is done with As/Bs: the tile is staged over them
   float* cs = reinterpret_cast<float*>(smem);
-  stage_tile<EPI, 64, 2, 2>(g, acc, cs, n0, wm * 32, wn * 32, lane);
+  stage_tile<EPI, 64, TM, 2>(g, acc, cs, n0, wm * (BM / 2), wn * 32, lane);
   __syncthreads();
-  store_tile<EPI, OutT, 64, 64>(g, cs, m0, n0, split, tid);
+  store_tile<EPI, OutT, BM, 64>(g, cs, m0, n0, split, tid);
 }
 
 // ------------------------------------------------------------- loop kernel
@@ -283,36 +295,35 @@ __global__ __launch_bounds__(256) void gemm_loop_kernel(GemmArgs g, int ks) {
   const T* A = static_cast<const T*>(g.A) + (size_t)split * ks;
   const T* Wt = static_cast<const T*>(g.W) + (size_t)split * ks;
 
+  // register staging of one BK-wide K tile (plain loops, no lambdas, so the
+  // arrays stay in registers)
   vec16 ra[A_IT], rb[B_IT];
-  auto fetch = [&](int kt) {
-    const int k0 = kt * BK;
-#pragma unroll
-    for (int i = 0; i < A_IT; ++i) {
-      int c = tid + i * 256, r = c / CPR, kc = (c % CPR) * VEC;
-      const int m = min(m0 + r, g.M - 1);
-      ra[i] = *reinterpret_cast<const vec16*>(A + (size_t)m * g.lda + k0 + kc);
-    }
-#pragma unroll
-    for (int i = 0; i < B_IT; ++i) {
-      int c = tid + i * 256, r = c / CPR, kc = (c % CPR) * VEC;
-      rb[i] = *reinterpret_cast<const vec16*>(Wt + (size_t)(n0 + r) * g.ldw + k0 + kc);
-    }
-  };
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < A_IT; ++i) {
-      int c = tid + i * 256, r = c / CPR, kc = (c % CPR) * VEC;
-      const bool live = m0 + r < g.M;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) ra[i].w[q] = live ? ra[i].w[q] : 0u;
-      *reinterpret_cast<vec16*>(&As[buf][r * LDK + kc]) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < B_IT; ++i) {
-      int c = tid + i * 256, r = c / CPR, kc = (c % CPR) * VEC;
-      *reinterpret_cast<vec16*>(&Bs[buf][r * LDK + kc]) = rb[i];
-    }
-  };
+#define SF_LOOP_FETCH(kt)                                                              \
+  {                                                                                    \
+    const int k0_ = (kt) * BK;                                                         \
+    _Pragma("unroll") for (int i = 0; i < A_IT; ++i) {                                 \
+      const int c = tid + i * 256, r = c / CPR, kc = (c % CPR) * VEC;                  \
+      ra[i] = *reinterpret_cast<const vec16*>(A + (size_t)min(m0 + r, g.M - 1) * g.lda + \
+                                              k0_ + kc);                               \
+    }                                                                                  \
+    _Pragma("unroll") for (int i = 0; i < B_IT; ++i) {                                 \
+      const int c = tid + i * 256, r = c / CPR, kc = (c % CPR) * VEC;                  \
+      rb[i] = *reinterpret_cast<const vec16*>(Wt + (size_t)(n0 + r) * g.ldw + k0_ + kc); \
+    }                                                                                  \
+  }
+#define SF_LOOP_STASH(buf)                                                             \
+  {                                                                                    \
+    _Pragma("unroll") for (int i = 0; i < A_IT; ++i) {                                 \
+      const int c = tid + i * 256, r = c / CPR, kc = (c % CPR) * VEC;                  \
+      const bool live = m0 + r < g.M;                                                  \
+      _Pragma("unroll") for (int q = 0; q < 4; ++q) ra[i].w[q] = live ? ra[i].w[q] : 0u; \
+      *reinterpret_cast<vec16*>(&As[buf][r * LDK + kc]) = ra[i];                       \
+    }                                                                                  \
+    _Pragma("unroll") for (int i = 0; i < B_IT; ++i) {                                 \
+      const int c = tid + i * 256, r = c / CPR, kc = (c % CPR) * VEC;                  \
+      *reinterpret_cast<vec16*>(&Bs[buf][r * LDK + kc]) = rb[i];                       \
+    }                                                                                  \
+  }
 
   f32x4 acc[TM][TN];
 #pragma unroll
@@ -321,12 +332,14 @@ __global__ __launch_bounds__(256) void gemm_loop_kernel(GemmArgs g, int ks) {
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nk = ks / BK;
-  fetch(0);
-  stash(0);
+  SF_LOOP_FETCH(0)
+  SF_LOOP_STASH(0)
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) fetch(kt + 1);
+    // the next tile (the last one again on the final iteration: unconditional
+    // loads and stores keep the staging arrays in registers)
+    SF_LOOP_FETCH(min(kt + 1, nk - 1))
 #pragma unroll
     for (int ks = 0; ks < BK / M_::KI; ++ks) {
       typename M_::frag af[TM], bfr[TN];
@@ -341,9 +354,11 @@ __global__ __launch_bounds__(256) void gemm_loop_kernel(GemmArgs g, int ks) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = M_::mma(af[i], bfr[j], acc[i][j]);
     }
-    if (kt + 1 < nk) stash(cur ^ 1);
+    SF_LOOP_STASH(cur ^ 1)
     __syncthreads();
   }
+#undef SF_LOOP_FETCH
+#undef SF_LOOP_STASH
   __syncthreads();
   float* cs = reinterpret_cast<float*>(smem);
   stage_tile<EPI, BN, TM, TN>(g, acc, cs, n0, wm * WM, wn * WN, lane);
@@ -393,13 +408,39 @@ static int n_slices(int K) {
   return ns;
 }
 
+// Residual-branch Linears (bf16, fp32 partials summed by the LayerNorm that
+// follows) are split over K more finely when N is narrow, so that a window of
+// a few hundred rows still fills about 32 tiles x slices per 64-row block:
+// the largest slice count up to that target whose slice width is supported.
+// Depends on K and N only, never on M.
+template <typename T>
+static int partial_slices(int K, int N) {
+  const int base = n_slices<T>(K);
+  if (sizeof(T) != 2) return base;
+  const int target = 32 / std::max(1, N / 64);
+  for (int ns = std::max(base, target); ns > base; --ns)
+    if (K % ns == 0 && slice_ok<T>(K / ns)) return ns;
+  return base;
+}
+
 // algorithmic work of the gemm() call being launched (for profiling)
 static thread_local double g_flops = 0, g_bytes = 0;
 
+// 64-row tiles, or 32-row tiles when 64-row ones would leave more than half
+// of the 256 CUs idle (the tile height does not change any result: every
+// output element accumulates the same K slice in the same order).
 template <typename T, typename OutT, int EPI, int KS>
 static void slice_launch(const GemmArgs& g, int ns, hipStream_t s) {
-  dim3 grid(g.N / 64, (g.M + 63) / 64, ns);
-  klaunch(PROF_GEMM, g_flops, g_bytes, gemm_slice_kernel<T, OutT, EPI, KS>, grid, dim3(256), s, g);
+  const int tiles64 = g.N / 64 * ((g.M + 63) / 64) * ns;
+  if (tiles64 < 128) {
+    dim3 grid(g.N / 64, (g.M + 31) / 32, ns);
+    klaunch(PROF_GEMM, g_flops, g_bytes, gemm_slice_kernel<T, OutT, EPI, KS, 32>, grid, dim3(256),
+            s, g);
+  } else {
+    dim3 grid(g.N / 64, (g.M + 63) / 64, ns);
+    klaunch(PROF_GEMM, g_flops, g_bytes, gemm_slice_kernel<T, OutT, EPI, KS, 64>, grid, dim3(256),
+            s, g);
+  }
 }
 
 template <typename T, typename OutT, int EPI>
@@ -430,7 +471,7 @@ static void launch_kernel(const GemmArgs& g, int ns, hipStream_t s) {
 
 template <typename T, typename OutT, int EPI>
 static int launch(const GemmArgs& g, hipStream_t s) {
-  const int ns = n_slices<T>(g.K);
+  const int ns = EPI == EPI_PARTIAL ? partial_slices<T>(g.K, g.N) : n_slices<T>(g.K);
   if (ns == 1 || EPI == EPI_PARTIAL) {
     if (ns > 1 && ns > g.max_split) return -1;
     launch_kernel<T, OutT, EPI>(g, ns, s);

@@ -72,6 +72,7 @@ static void ln_launch(const LnArgs& a, dim3 grid, hipStream_t s, double by) {
     case 2: klaunch(PROF_LN, 0.0, by, ln_kernel<T, D, 2>, grid, dim3(256), s, a); break;
     case 3: klaunch(PROF_LN, 0.0, by, ln_kernel<T, D, 3>, grid, dim3(256), s, a); break;
     case 4: klaunch(PROF_LN, 0.0, by, ln_kernel<T, D, 4>, grid, dim3(256), s, a); break;
+    case 6: klaunch(PROF_LN, 0.0, by, ln_kernel<T, D, 6>, grid, dim3(256), s, a); break;
     case 8: klaunch(PROF_LN, 0.0, by, ln_kernel<T, D, 8>, grid, dim3(256), s, a); break;
     default: break;  // rejected by layernorm()
   }
@@ -80,7 +81,7 @@ static void ln_launch(const LnArgs& a, dim3 grid, hipStream_t s, double by) {
 void layernorm(const LnArgs& a, bool bf16, hipStream_t s) {
   if (a.M <= 0) return;
   const int ns = a.part ? a.nsplit : 0;
-  if (ns < 0 || ns == 5 || ns == 6 || ns == 7 || ns > 8 || (ns > 0 && !a.pbias)) {
+  if (ns < 0 || ns == 5 || ns == 7 || ns > 8 || (ns > 0 && !a.pbias)) {
     flag_launch_failure();
     return;
   }
@@ -99,29 +100,59 @@ void layernorm(const LnArgs& a, bool bf16, hipStream_t s) {
 // ------------------------------------------- conformer depthwise conv (k=9)
 // out[t,c] = swish(scale[c] * sum_k w[c,k] g[t+k-4,c] + shift[c]); rows at or
 // beyond n_valid (and outside the window) count as zero. BatchNorm and the
-// conv bias are folded into scale/shift.
+// conv bias are folded into scale/shift. One workgroup = DW_ROWS frames of
+// one stream; a thread owns 4 channels and keeps the DW_ROWS + 8 input rows
+// of them in registers (16-byte loads, each input row loaded once).
+#define DW_ROWS 4
 template <typename T>
-__global__ __launch_bounds__(256) void dwconv_time_kernel(const float* glu, int W, int n_valid,
+__global__ __launch_bounds__(128) void dwconv_time_kernel(const float* glu, int W, int n_valid,
                                                           const float* w9, const float* sc,
                                                           const float* sh, T* out) {
-  const int t = blockIdx.x, b = blockIdx.y;
-  const float* gb = glu + (size_t)b * W * 512;
+  const int t0 = blockIdx.x * DW_ROWS, b = blockIdx.y, c = threadIdx.x * 4;
+  const float* gb = glu + (size_t)b * W * 512 + c;
+  float4 x[DW_ROWS + 8];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int c = threadIdx.x + 256 * h;
-    float x[9];
+  for (int j = 0; j < DW_ROWS + 8; ++j)
+    x[j] = *reinterpret_cast<const float4*>(gb + (size_t)min(max(t0 + j - 4, 0), W - 1) * 512);
+  float4 wk[9];  // w[c..c+3][k] for tap k, from the [c][9] layout
+  {
+    float wr[36];
 #pragma unroll
-    for (int k = 0; k < 9; ++k) {
-      const int tt = min(max(t + k - 4, 0), W - 1);
-      x[k] = gb[(size_t)tt * 512 + c];
+    for (int q = 0; q < 9; ++q) {
+      const float4 v = *reinterpret_cast<const float4*>(w9 + c * 9 + 4 * q);
+      wr[4 * q] = v.x; wr[4 * q + 1] = v.y; wr[4 * q + 2] = v.z; wr[4 * q + 3] = v.w;
     }
-    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < 9; ++k) wk[k] = make_float4(wr[k], wr[9 + k], wr[18 + k], wr[27 + k]);
+  }
+  const float4 s4 = *reinterpret_cast<const float4*>(sc + c);
+  const float4 h4 = *reinterpret_cast<const float4*>(sh + c);
+#pragma unroll
+  for (int r = 0; r < DW_ROWS; ++r) {
+    const int t = t0 + r;
+    if (t >= W) break;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int k = 0; k < 9; ++k) {
       const int tt = t + k - 4;
-      acc += (tt >= 0 && tt < n_valid) ? w9[c * 9 + k] * x[k] : 0.f;
+      const bool live = tt >= 0 && tt < n_valid;
+      const float4 v = x[r + k];
+      acc.x += live ? wk[k].x * v.x : 0.f;
+      acc.y += live ? wk[k].y * v.y : 0.f;
+      acc.z += live ? wk[k].z * v.z : 0.f;
+      acc.w += live ? wk[k].w * v.w : 0.f;
     }
-    out[((size_t)b * W + t) * 512 + c] = from_f<T>(swishf_(sc[c] * acc + sh[c]));
+    float y[4] = {swishf_(s4.x * acc.x + h4.x), swishf_(s4.y * acc.y + h4.y),
+                  swishf_(s4.z * acc.z + h4.z), swishf_(s4.w * acc.w + h4.w)};
+    T* o = out + ((size_t)b * W + t) * 512 + c;
+    if constexpr (sizeof(T) == 2) {
+      uint2 u;
+      u.x = (uint32_t)f2bf(y[0]) | ((uint32_t)f2bf(y[1]) << 16);
+      u.y = (uint32_t)f2bf(y[2]) | ((uint32_t)f2bf(y[3]) << 16);
+      *reinterpret_cast<uint2*>(o) = u;
+    } else {
+      *reinterpret_cast<float4*>(o) = make_float4(y[0], y[1], y[2], y[3]);
+    }
   }
 }
 
@@ -129,12 +160,12 @@ void dwconv_time(const float* glu, int B, int W, int n_valid, const float* w9, c
                  const float* sh, void* out, bool bf16, hipStream_t s) {
   if (W <= 0) return;
   const double fl = 2.0 * 9 * 512 * B * W, by = (double)B * W * 512 * (4.0 + (bf16 ? 2 : 4));
-  dim3 grid(W, B);
+  dim3 grid((W + DW_ROWS - 1) / DW_ROWS, B);
   if (bf16)
-    klaunch(PROF_CONV, fl, by, dwconv_time_kernel<bf16_t>, grid, dim3(256), s, glu, W, n_valid, w9,
+    klaunch(PROF_CONV, fl, by, dwconv_time_kernel<bf16_t>, grid, dim3(128), s, glu, W, n_valid, w9,
             sc, sh, static_cast<bf16_t*>(out));
   else
-    klaunch(PROF_CONV, fl, by, dwconv_time_kernel<float>, grid, dim3(256), s, glu, W, n_valid, w9,
+    klaunch(PROF_CONV, fl, by, dwconv_time_kernel<float>, grid, dim3(128), s, glu, W, n_valid, w9,
             sc, sh, static_cast<float*>(out));
 }
 
@@ -327,31 +358,55 @@ void stack8(const float* mel, long long mel_bstride, int mel_base, int T, int e0
 }
 
 // --------------------------------------------------------------- heads
-// Sortformer head, fp32: sigmoid(W2 relu(W1 x + b1) + b2), 8 rows per block.
-__global__ __launch_bounds__(192) void head_sf_kernel(const float* x, int M, const float* w1t,
+// Sortformer head, fp32: sigmoid(W2 relu(W1 x + b1) + b2). One workgroup =
+// 16 rows: the 192x192 layer runs on fp32 MFMA (wave w computes output
+// columns 48w..48w+47, A rows from LDS, W1^T read straight from global), the
+// 192->S layer and the sigmoid on the vector units.
+__global__ __launch_bounds__(256) void head_sf_kernel(const float* x, int M, const float* w1t,
                                                       const float* b1, const float* w2,
                                                       const float* b2, int S, float* probs) {
-  __shared__ float xs[8][192], hs[8][192];
-  const int r0 = blockIdx.x * 8, t = threadIdx.x;
-  float xv[8];
+  __shared__ float xs[16][196], hs[16][196];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r0 = blockIdx.x * 16;
+  const int c16 = lane & 15, kq = lane >> 4;
+  {
+    float4 v[3];
 #pragma unroll
-  for (int r = 0; r < 8; ++r) xv[r] = x[(size_t)min(r0 + r, M - 1) * 192 + t];
+    for (int q = 0; q < 3; ++q) {  // 16 rows x 48 float4 = 3 per thread
+      const int i = tid + 256 * q, r = i / 48, c = (i % 48) * 4;
+      v[q] = *reinterpret_cast<const float4*>(x + (size_t)min(r0 + r, M - 1) * 192 + c);
+    }
 #pragma unroll
-  for (int r = 0; r < 8; ++r) xs[r][t] = r0 + r < M ? xv[r] : 0.f;
+    for (int q = 0; q < 3; ++q) {
+      const int i = tid + 256 * q, r = i / 48, c = (i % 48) * 4;
+      const bool live = r0 + r < M;
+      xs[r][c] = live ? v[q].x : 0.f;
+      xs[r][c + 1] = live ? v[q].y : 0.f;
+      xs[r][c + 2] = live ? v[q].z : 0.f;
+      xs[r][c + 3] = live ? v[q].w : 0.f;
+    }
+  }
   __syncthreads();
-  float acc[8];
+  f32x4 acc[3];
 #pragma unroll
-  for (int r = 0; r < 8; ++r) acc[r] = b1[t];
-  for (int k = 0; k < 192; ++k) {
-    const float wv = w1t[k * 192 + t];
+  for (int j = 0; j < 3; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+  for (int k = 0; k < 192; k += 4) {
+    const float av = xs[c16][k + kq];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) acc[r] += xs[r][k] * wv;
+    for (int j = 0; j < 3; ++j)
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, w1t[(k + kq) * 192 + 48 * w + 16 * j + c16],
+                                                    acc[j], 0, 0, 0);
   }
 #pragma unroll
-  for (int r = 0; r < 8; ++r) hs[r][t] = fmaxf(acc[r], 0.f);
+  for (int j = 0; j < 3; ++j) {
+    const int n = 48 * w + 16 * j + c16;
+    const float bn = b1[n];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hs[4 * kq + i][n] = fmaxf(acc[j][i] + bn, 0.f);
+  }
   __syncthreads();
-  if (t < 8 * S) {
-    const int r = t / S, sp = t % S;
+  if (tid < 16 * S) {
+    const int r = tid / S, sp = tid % S;
     if (r0 + r < M) {
       float z = b2[sp];
       for (int k = 0; k < 192; ++k) z += hs[r][k] * w2[sp * 192 + k];
@@ -363,7 +418,7 @@ __global__ __launch_bounds__(192) void head_sf_kernel(const float* x, int M, con
 void head_sortformer(const float* x, int M, const float* w1t, const float* b1, const float* w2,
                      const float* b2, int S, float* probs, hipStream_t s) {
   if (M <= 0) return;
-  hipLaunchKernelGGL(head_sf_kernel, dim3((M + 7) / 8), dim3(192), 0, s, x, M, w1t, b1, w2, b2, S,
+  hipLaunchKernelGGL(head_sf_kernel, dim3((M + 15) / 16), dim3(256), 0, s, x, M, w1t, b1, w2, b2, S,
                      probs);
 }
 
