@@ -471,7 +471,13 @@ static void launch_kernel(const GemmArgs& g, int ns, hipStream_t s) {
 
 template <typename T, typename OutT, int EPI>
 static int launch(const GemmArgs& g, hipStream_t s) {
-  const int ns = EPI == EPI_PARTIAL ? partial_slices<T>(g.K, g.N) : n_slices<T>(g.K);
+  // Windows of a few thousand rows: K slices as above (at most 512 wide; finer
+  // for narrow residual branches). Larger problems fill the GPU with row tiles
+  // alone and run the whole K in one loop. The choice depends on the problem
+  // size, not on its content: within each regime a row's result does not
+  // depend on how many rows share the launch.
+  const int ns = g.M > SLICE_MAX_ROWS ? 1
+                 : EPI == EPI_PARTIAL ? partial_slices<T>(g.K, g.N) : n_slices<T>(g.K);
   if (ns == 1 || EPI == EPI_PARTIAL) {
     if (ns > 1 && ns > g.max_split) return -1;
     launch_kernel<T, OutT, EPI>(g, ns, s);

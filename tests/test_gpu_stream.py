@@ -168,10 +168,7 @@ def test_stream_errors_reset_and_determinism(rt, sf, sfbf):
     assert np.array_equal(a, b)
 
 
-def test_lockstep_batch_matches_single_streams(rt, sfbf):
-    """Ultra-low preset, 64 streams in lockstep: every stream equals the
-    same stream run alone (first 30 steps)."""
-    B, steps = 64, 30
+def _lockstep(sfbf, B, steps, check):
     n = 1280 * (steps * 3 + 1) + 40
     audio = np.stack([workload_audio("ultralow64x120s", stream=b, seconds=n / 16000 + 1)[:n]
                       for b in range(B)])
@@ -182,7 +179,7 @@ def test_lockstep_batch_matches_single_streams(rt, sfbf):
         outs.append(st.step(_cuda(audio[:, pos:pos + k])).clone())
         pos += k
     got = torch.cat(outs, 1).cpu().numpy()
-    for b in (0, 37, 63):
+    for b in check:
         one = sfbf.stream("ultra_low", batch=1)
         o, pos = [], 0
         for s in range(steps):
@@ -190,8 +187,26 @@ def test_lockstep_batch_matches_single_streams(rt, sfbf):
             o.append(one.step(_cuda(audio[b:b + 1, pos:pos + k])).clone())
             pos += k
         single = torch.cat(o, 1)[0].cpu().numpy()
-        err, _ = _report(f"lockstep b={b}", got[b], single)
-        assert err <= 1e-6
+        yield b, got[b], single
+
+
+def test_lockstep_small_batch_is_bit_exact(rt, sfbf):
+    """Ultra-low preset, 6 streams in lockstep (every window under 4096 rows,
+    the GEMMs' K slicing is the single-stream one): each stream equals the
+    same stream run alone, bit for bit."""
+    for b, got, single in _lockstep(sfbf, 6, 30, (0, 5)):
+        err, _ = _report(f"lockstep B=6 b={b}", got, single)
+        assert err == 0.0
+
+
+def test_lockstep_batch_matches_single_streams(rt, sfbf):
+    """Ultra-low preset, 64 streams in lockstep (30 steps): once the batched
+    window exceeds 4096 rows the GEMMs run the whole K in one loop instead of
+    the single stream's K slices, so each stream agrees with its solo run to
+    the bf16 parity bar rather than bit for bit."""
+    for b, got, single in _lockstep(sfbf, 64, 30, (0, 37, 63)):
+        err, agree = _report(f"lockstep B=64 b={b}", got, single)
+        assert err <= 2e-2 and agree >= 0.995
 
 
 def test_ultra_low_batched_vs_oracle_first_steps(rt, sfbf):
