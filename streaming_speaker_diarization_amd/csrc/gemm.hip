@@ -366,6 +366,130 @@ __global__ __launch_bounds__(256) void gemm_loop_kernel(GemmArgs g, int ks) {
   store_tile<EPI, OutT, BM, BN>(g, cs, m0, n0, split, tid);
 }
 
+// ----------------------------------------------------- large-M bf16 kernel
+// Batched windows (tens of thousands of rows). 128 x BN tile, 4 waves in a
+// 2 x 2 grid (64 x BN/2 each), K in BK-wide tiles through an NST-deep LDS
+// ring filled by LDS-DMA loads (global_load_lds_dwordx4: lane l's 16 bytes
+// land at the wave's LDS block base + 16 l), so the loads for tile kt+NST-1
+// are in flight while tile kt is multiplied, with no register staging. A tile row is BK/8 chunks of 16
+// bytes; chunk c of row r sits at chunk position c ^ (r mod BK/8) so the 16
+// rows one MFMA fragment read touches spread over the banks. Rows past M load
+// a clamped row: their outputs are never stored. Workgroups are mapped to
+// tiles so that each XCD (dispatch round robin over 8) owns a contiguous range
+// of row blocks and its L2 fetches each A row block once.
+__device__ __forceinline__ void lds_dma16(const void* g, void* lds_block) {
+  __builtin_amdgcn_global_load_lds(g, lds_block, 16, 0, 0);
+}
+
+// vmcnt-only wait (expcnt / lgkmcnt left unconstrained), n < 64
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <typename OutT, int EPI, int BN, int BK, int NST>
+__global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs g) {
+  using M_ = MF<bf16_t>;
+  constexpr int BM = 128;
+  constexpr int TM = 4, TN = BN / 32;                 // 16x16 tiles per wave
+  constexpr int CPR = BK / 8;                         // 16-byte chunks per tile row
+  constexpr int RPB = 64 / CPR;                       // tile rows per 1 KB DMA block
+  constexpr int A_BLK = BM / RPB, B_BLK = BN / RPB;
+  constexpr int STAGE = (BM + BN) * BK * 2;           // bytes per ring stage
+  constexpr int LOADS = (A_BLK + B_BLK) / 4;          // LDS-DMA loads per wave per stage
+  static_assert((A_BLK + B_BLK) % 4 == 0, "stage split over the waves");
+  constexpr int RING = NST * STAGE, ST = stage_bytes<EPI, BM, BN>();
+  __shared__ __align__(16) char smem[RING > ST ? RING : ST];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // XCD-aware tile order (bijection over the grid): physical workgroup i runs
+  // on XCD i % 8; XCD x takes logical tiles [x*q + min(x, r), ... + q + (x < r)).
+  const int gx = gridDim.x, total = gx * gridDim.y;
+  const int pid = blockIdx.x + gx * blockIdx.y;
+  const int q8 = total / 8, r8 = total % 8, xcd = pid % 8;
+  const int t = xcd * q8 + min(xcd, r8) + pid / 8;
+  const int n0 = (t % gx) * BN, m0 = (t / gx) * BM;
+
+  const bf16_t* A = static_cast<const bf16_t*>(g.A);
+  const bf16_t* Wt = static_cast<const bf16_t*>(g.W);
+  // this lane's row within a DMA block and the global chunk it fetches
+  const int lr = lane / CPR, lc = (lane % CPR) ^ (lr % CPR);
+  auto issue = [&](int kt) {
+    char* st = smem + (kt % NST) * STAGE;
+    const int k0 = kt * BK + lc * 8;
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int blk = wave * LOADS + j;  // A blocks first, then B blocks
+      if (blk < A_BLK) {
+        const int r = min(m0 + blk * RPB + lr, g.M - 1);
+        lds_dma16(A + (size_t)r * g.lda + k0, st + blk * 1024);
+      } else {
+        const int r = n0 + (blk - A_BLK) * RPB + lr;
+        lds_dma16(Wt + (size_t)r * g.ldw + k0, st + blk * 1024);
+      }
+    }
+  };
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = g.K / BK;
+#pragma unroll
+  for (int p = 0; p < NST - 1; ++p)
+    if (p < nk) issue(p);
+  const int fr = lane & 15, fq = lane >> 4;  // fragment row, k-chunk within a 32-wide step
+  for (int kt = 0; kt < nk; ++kt) {
+    // tile kt's loads are this wave's oldest outstanding ones
+    if constexpr (NST >= 3) {
+      if (kt + NST - 2 < nk) wait_vm<(NST - 2) * LOADS>();
+      else if (kt + 1 < nk) wait_vm<LOADS>();
+      else wait_vm<0>();
+    } else {
+      wait_vm<0>();
+    }
+    // every wave's part of tile kt is in LDS and tile kt-1's reads are done;
+    // a bare barrier: __syncthreads() would also wait for the later tiles'
+    // loads still in flight
+    __builtin_amdgcn_s_barrier();
+    if (kt + NST - 1 < nk) issue(kt + NST - 1);
+    const char* st = smem + (kt % NST) * STAGE;
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      const int c = ks * 4 + fq;  // 16-byte chunk of the fragment's 8 k values
+      M_::frag af[TM], bfr[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int r = wm * 64 + 16 * i + fr;
+        af[i] = *reinterpret_cast<const bf16x8_t*>(st + r * (BK * 2) + ((c ^ (r % CPR)) << 4));
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int r = wn * (BN / 2) + 16 * j + fr;
+        bfr[j] = *reinterpret_cast<const bf16x8_t*>(st + BM * BK * 2 + r * (BK * 2) +
+                                                    ((c ^ (r % CPR)) << 4));
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = M_::mma(af[i], bfr[j], acc[i][j]);
+    }
+  }
+  __syncthreads();  // the ring is reused for the staged epilogue
+  float* cs = reinterpret_cast<float*>(smem);
+  stage_tile<EPI, BN, TM, TN>(g, acc, cs, n0, wm * 64, wn * (BN / 2), lane);
+  __syncthreads();
+  store_tile<EPI, OutT, BM, BN>(g, cs, m0, n0, 0, tid);
+}
+
+// 64-wide K tiles, double-buffered: with the 68 KB epilogue tile two
+// workgroups fit on a CU, which measured faster than deeper rings with one
+#define SF_BIG_BK 64
+#define SF_BIG_NST 2
+
 // ------------------------------------------------- split-K reduce + epilogue
 // v = sum_s part[s][m][n] (in split order) + bias[n], then the epilogue.
 template <typename OutT, int EPI>
@@ -457,6 +581,15 @@ static void launch_kernel(const GemmArgs& g, int ns, hipStream_t s) {
           if (ks == 384) slice_launch<T, OutT, EPI, 384>(g, ns, s);
           else slice_launch<T, OutT, EPI, 512>(g, ns, s);
         }
+    }
+  } else if (sizeof(T) == 2 && ns == 1 && g.K % SF_BIG_BK == 0 && g.N % 64 == 0) {
+    if constexpr (sizeof(T) == 2) {
+      if (g.N % 128 == 0)
+        klaunch(PROF_GEMM, g_flops, g_bytes, gemm_big_kernel<OutT, EPI, 128, SF_BIG_BK, SF_BIG_NST>,
+                dim3(g.N / 128, (g.M + 127) / 128), dim3(256), s, g);
+      else
+        klaunch(PROF_GEMM, g_flops, g_bytes, gemm_big_kernel<OutT, EPI, 64, SF_BIG_BK, SF_BIG_NST>,
+                dim3(g.N / 64, (g.M + 127) / 128), dim3(256), s, g);
     }
   } else if (g.M > 1536 && g.N % 128 == 0) {
     dim3 grid(g.N / 128, (g.M + 127) / 128, ns);
