@@ -341,6 +341,226 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Throughput form for batched windows (streams x window above 4096 rows),
+// bf16: one workgroup = 64 query rows (16 per wave) of one (stream, head).
+// The four waves share each 64-key tile of K, V^T and (relative positions)
+// the 128-row band of p(delta) the tile's (i, j) pairs touch, staged once in
+// LDS per tile while the next tile's loads are in flight in registers; each
+// wave runs the online softmax over all tiles for its own rows. Same
+// arithmetic per tile as the latency form above; only the order in which the
+// key tiles are combined differs.
+template <int HD, int MODE>
+__global__ __launch_bounds__(256) void attn_tp_kernel(AttnArgs a) {
+  using M_ = MF<bf16_t>;
+  constexpr int HDP = HD <= 32 ? 32 : 64;  // head dim padded for MFMA
+  constexpr int NQF = HDP / 32;            // k-steps over head dims
+  constexpr int NDT = HDP / 16;            // output column tiles
+  constexpr int LK = HDP + 8;              // K / band row pitch (bf16)
+  constexpr int LV = 64 + 8;               // V^T row pitch
+  constexpr int LDP = 72;
+  constexpr bool REL = MODE == ATT_RELPOS;
+  constexpr int NB = REL ? 128 : 0;        // band rows per tile
+  constexpr int CPK = HDP / 8;             // 16-byte chunks per K / band row
+  constexpr int NCK = 64 * CPK / 256, NCV = HDP * 8 / 256, NCB = NB * CPK / 256;
+  static_assert(MODE != ATT_ROPE, "rotary layers use the latency form");
+  __shared__ __align__(16) bf16_t Ks[64 * LK];
+  __shared__ __align__(16) bf16_t Vs[HDP * LV];
+  __shared__ __align__(16) bf16_t Bs[REL ? NB * LK : 8];
+  __shared__ float Gs[REL ? 4 * 16 * 81 : 1];
+  __shared__ __align__(16) bf16_t Ps[4 * 16 * LDP];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int iq0 = blockIdx.x * 64, h = blockIdx.y, b = blockIdx.z;
+  const int iw = iq0 + 16 * w;  // this wave's first query row
+  const bf16_t* qkv = static_cast<const bf16_t*>(a.qkv);
+  const size_t rowbase = (size_t)b * a.W;
+  const float sl2 = a.scale * 1.4426950408889634f;
+  const bf16_t* vtb = static_cast<const bf16_t*>(a.vt) + (size_t)(b * a.H + h) * HD * a.vpitch;
+  const bf16_t* P = static_cast<const bf16_t*>(a.P);
+
+  // ---- query fragments of row iw + c16 (element e of fragment ks is dim
+  // ks*32 + 8g + e), with the u / v biases for relative positions
+  bf16x8_t qa[NQF], qb[NQF];
+  {
+    const int qi = iw + c16, qc = min(qi, a.W - 1);
+#pragma unroll
+    for (int ks = 0; ks < NQF; ++ks) {
+      float ua[8], va[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = ks * 32 + 8 * g + e, dc = min(d, HD - 1);
+        float q = bf2f(qkv[(rowbase + qc) * a.ldq + a.qoff + h * HD + dc]);
+        q = (qi < a.W && d < HD) ? q : 0.f;
+        ua[e] = q;
+        va[e] = q;
+        if constexpr (REL) {
+          ua[e] += d < HD ? a.ub[h * HD + dc] : 0.f;
+          va[e] += d < HD ? a.vb[h * HD + dc] : 0.f;
+        }
+      }
+      qa[ks] = Pack<bf16_t>::make(ua);
+      qb[ks] = Pack<bf16_t>::make(va);
+    }
+  }
+
+  // ---- one tile's K, V^T and band chunks into registers (clamped, unconditional)
+  vec16 rk[NCK], rv[NCV], rbd[NCB > 0 ? NCB : 1];
+  auto fetch = [&](int j0) {
+#pragma unroll
+    for (int i = 0; i < NCK; ++i) {
+      const int c = tid + 256 * i, r = c / CPK, q = c % CPK;
+      const int j = min(j0 + r, a.W - 1), d = min(8 * q, (HD / 8 - 1) * 8);
+      rk[i] = *reinterpret_cast<const vec16*>(qkv + (rowbase + j) * a.ldq + a.koff + h * HD + d);
+    }
+#pragma unroll
+    for (int i = 0; i < NCV; ++i) {
+      const int c = tid + 256 * i, d = c / 8, q = c % 8;
+      rv[i] = *reinterpret_cast<const vec16*>(vtb + (size_t)min(d, HD - 1) * a.vpitch +
+                                               min(j0 + 8 * q, a.vpitch - 8));
+    }
+#pragma unroll
+    for (int i = 0; i < NCB; ++i) {
+      const int c = tid + 256 * i, r = c / CPK, q = c % CPK;
+      const int pr = min(max(iq0 - j0 - 63 + r + a.p_center, 0), 2 * a.p_center);
+      rbd[i] = *reinterpret_cast<const vec16*>(P + (size_t)pr * a.ldp + h * HD + 8 * q);
+    }
+  };
+  // zero what lies outside the head, the window or the position table
+  auto stash = [&](int j0) {
+#pragma unroll
+    for (int i = 0; i < NCK; ++i) {
+      const int c = tid + 256 * i, r = c / CPK, q = c % CPK;
+      const bool live = 8 * q < HD;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rk[i].w[e] = live ? rk[i].w[e] : 0u;
+      *reinterpret_cast<vec16*>(&Ks[r * LK + 8 * q]) = rk[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NCV; ++i) {
+      const int c = tid + 256 * i, d = c / 8, q = c % 8, j = j0 + 8 * q;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t v = d < HD ? rv[i].w[e] : 0u;
+        const uint32_t lo = j + 2 * e < a.W ? (v & 0xFFFFu) : 0u;
+        const uint32_t hi = j + 2 * e + 1 < a.W ? (v & 0xFFFF0000u) : 0u;
+        rv[i].w[e] = lo | hi;
+      }
+      *reinterpret_cast<vec16*>(&Vs[d * LV + 8 * q]) = rv[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NCB; ++i) {
+      const int c = tid + 256 * i, r = c / CPK, q = c % CPK;
+      const int dl = iq0 - j0 - 63 + r;
+      const bool live = dl >= -a.p_center && dl <= a.p_center && 8 * q < HD;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rbd[i].w[e] = live ? rbd[i].w[e] : 0u;
+      *reinterpret_cast<vec16*>(&Bs[r * LK + 8 * q]) = rbd[i];
+    }
+  };
+
+  f32x4 O[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mrow[4], lrow[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) { mrow[r] = -INFINITY; lrow[r] = 0.f; }
+
+  const int ntile = (a.n_valid + 63) / 64;
+  fetch(0);
+  for (int kt = 0; kt < ntile; ++kt) {
+    const int j0 = kt * 64;
+    __syncthreads();  // every wave is done with the previous tile
+    stash(j0);
+    __syncthreads();
+    // next tile (this one again on the last step: unconditional loads keep the
+    // staging arrays in registers), in flight while this tile is used
+    fetch(min(j0 + 64, (ntile - 1) * 64));
+
+    // ---- scores
+    f32x4 S[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      S[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NQF; ++ks)
+        S[nt] = M_::mma(qa[ks], *reinterpret_cast<const bf16x8_t*>(
+                                    &Ks[(16 * nt + c16) * LK + ks * 32 + 8 * g]), S[nt]);
+    }
+    if constexpr (REL) {
+      // G[i][c] = (q_i+v).p(delta), band row 16w + c <-> delta iw-j0-63+c;
+      // the score of (i, j) takes column i-j+63
+      float* G = &Gs[w * 16 * 81];
+#pragma unroll
+      for (int ct = 0; ct < 5; ++ct) {
+        f32x4 acc{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NQF; ++ks)
+          acc = M_::mma(qb[ks], *reinterpret_cast<const bf16x8_t*>(
+                                    &Bs[(16 * w + 16 * ct + c16) * LK + ks * 32 + 8 * g]), acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) G[(4 * g + r) * 81 + 16 * ct + c16] = acc[r];
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          S[nt][r] += G[(4 * g + r) * 81 + (4 * g + r) - (16 * nt + c16) + 63];
+    }
+
+    // ---- online softmax (log2 domain)
+    float mx[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mx[r] = -INFINITY;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const bool valid = j0 + 16 * nt + c16 < a.n_valid;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        S[nt][r] = valid ? S[nt][r] * sl2 : -INFINITY;
+        mx[r] = fmaxf(mx[r], S[nt][r]);
+      }
+    }
+    bf16_t* Pw = &Ps[w * 16 * LDP];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float mnew = fmaxf(mrow[r], row16_max(mx[r]));
+      const float alpha = exp2f(mrow[r] - mnew);
+      float rs = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const float p = exp2f(S[nt][r] - mnew);
+        rs += p;
+        Pw[(4 * g + r) * LDP + 16 * nt + c16] = f2bf(p);
+      }
+      lrow[r] = lrow[r] * alpha + row16_sum(rs);
+      mrow[r] = mnew;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) O[dt][r] *= alpha;
+    }
+    wave_lds_sync();
+    // ---- O += P.V
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const auto pa = M_::ld(&Pw[c16 * LDP + ks * 32], lane);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        O[dt] = M_::mma(pa, *reinterpret_cast<const bf16x8_t*>(
+                                &Vs[(16 * dt + c16) * LV + ks * 32 + 8 * g]), O[dt]);
+    }
+  }
+
+  bf16_t* ctx = static_cast<bf16_t*>(a.ctx);
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = iw + 4 * g + r, d = 16 * dt + c16;
+      if (i < a.W && d < HD) ctx[(rowbase + i) * a.ldc + h * HD + d] = f2bf(O[dt][r] / lrow[r]);
+    }
+}
+
 template <typename T, int NW>
 static void launch_attn_nw(const AttnArgs& a, int mode, int hd, hipStream_t s, double fl, double by) {
   dim3 grid((a.W + 15) / 16, a.H, a.B), block(NW * 64);
@@ -363,6 +583,14 @@ static void launch_attn(const AttnArgs& a, int mode, int hd, hipStream_t s, doub
   launch_attn_nw<T, 4>(a, mode, hd, s, fl, by);
 }
 
+// Latency form for single windows and small batches; the throughput form
+// once streams x window exceeds 4096 rows (the row count at which the GEMMs
+// switch to whole-K loops too).
+static bool use_tp(const AttnArgs& a, int mode, int hd, bool bf16) {
+  return bf16 && (long long)a.B * a.W > 4096 &&
+         ((mode == ATT_RELPOS && hd == 64) || (mode == ATT_PLAIN && hd == 24));
+}
+
 void attention(const AttnArgs& a, int mode, int head_dim, bool bf16, hipStream_t s) {
   if (a.W <= 0 || a.B <= 0) return;
   // scores (q.k), the relative-position term (q.p(i-j)) and P.V per head
@@ -370,8 +598,17 @@ void attention(const AttnArgs& a, int mode, int head_dim, bool bf16, hipStream_t
   const double es = bf16 ? 2 : 4;
   const double fl = pairs * 2.0 * head_dim * (mode == ATT_RELPOS ? 3 : 2);
   const double by = es * a.B * a.W * a.H * head_dim * 4.0;
-  if (bf16) launch_attn<bf16_t>(a, mode, head_dim, s, fl, by);
-  else launch_attn<float>(a, mode, head_dim, s, fl, by);
+  if (use_tp(a, mode, head_dim, bf16)) {
+    dim3 grid((a.W + 63) / 64, a.H, a.B);
+    if (mode == ATT_RELPOS)
+      klaunch(PROF_ATTN, fl, by, attn_tp_kernel<64, ATT_RELPOS>, grid, dim3(256), s, a);
+    else
+      klaunch(PROF_ATTN, fl, by, attn_tp_kernel<24, ATT_PLAIN>, grid, dim3(256), s, a);
+  } else if (bf16) {
+    launch_attn<bf16_t>(a, mode, head_dim, s, fl, by);
+  } else {
+    launch_attn<float>(a, mode, head_dim, s, fl, by);
+  }
 }
 
 }  // namespace sf
