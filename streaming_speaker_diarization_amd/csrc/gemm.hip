@@ -14,6 +14,8 @@
 //    sums, reduced in a fixed order (deterministic) by the consumer.
 //  * loop kernel (large batched windows): BMxBN tiles, BK-column K tiles
 //    double-buffered through registers and LDS.
+#include <utility>
+
 #include "kernels.h"
 
 namespace sf {
@@ -381,6 +383,12 @@ __device__ __forceinline__ void lds_dma16(const void* g, void* lds_block) {
   __builtin_amdgcn_global_load_lds(g, lds_block, 16, 0, 0);
 }
 
+// f(integral_constant<int, I>) for every I of the sequence, in order
+template <typename F, int... I>
+__device__ __forceinline__ void for_each_index(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+
 // vmcnt-only wait (expcnt / lgkmcnt left unconstrained), n < 64
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -490,6 +498,87 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs g) {
 #define SF_BIG_BK 64
 #define SF_BIG_NST 2
 
+// ------------------------------------------------ slice kernel, bf16 form
+// Same tiling and K-slice as gemm_slice_kernel, but the slice arrives by
+// LDS-DMA in 64-wide K phases (every phase's loads issued at once, no register
+// staging): the MFMAs of phase p run while phases p+1.. are still landing.
+// Each 64-wide phase row is 8 chunks of 16 bytes, chunk c of row r stored at
+// position c ^ (r & 7); one 1 KB DMA block holds 8 rows.
+template <typename OutT, int EPI, int KS, int BM>
+__global__ __launch_bounds__(256) void gemm_slice_dma_kernel(GemmArgs g) {
+  using M_ = MF<bf16_t>;
+  constexpr int NPH = KS / 64;                  // K phases
+  constexpr int PH = (BM + 64) * 128;           // bytes per phase (A rows, then W rows)
+  constexpr int LOADS = (BM + 64) / 8 / 4;      // DMA blocks per wave per phase
+  constexpr int TM = BM / 32;                   // 16-row MFMA tiles per wave (waves 2 x 2)
+  static_assert(KS % 64 == 0 && (BM + 64) % 32 == 0, "slice shape");
+  constexpr int AB = NPH * PH, ST = stage_bytes<EPI, BM, 64>();
+  __shared__ __align__(16) char smem[AB > ST ? AB : ST];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int n0 = blockIdx.x * 64, m0 = blockIdx.y * BM, split = blockIdx.z;
+  const int k0 = split * KS;
+  const bf16_t* A = static_cast<const bf16_t*>(g.A);
+  const bf16_t* Wt = static_cast<const bf16_t*>(g.W);
+
+  const int lr = lane >> 3, lc = (lane & 7) ^ lr;  // row in a DMA block, chunk fetched
+#pragma unroll
+  for (int p = 0; p < NPH; ++p) {
+    char* ph = smem + p * PH;
+    const int kk = k0 + p * 64 + lc * 8;
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int blk = wave * LOADS + j;  // A blocks first, then W blocks
+      if (blk < BM / 8) {
+        const int r = min(m0 + blk * 8 + lr, g.M - 1);
+        lds_dma16(A + (size_t)r * g.lda + kk, ph + blk * 1024);
+      } else {
+        const int r = n0 + (blk - BM / 8) * 8 + lr;
+        lds_dma16(Wt + (size_t)r * g.ldw + kk, ph + blk * 1024);
+      }
+    }
+  }
+
+  f32x4 acc[TM][2];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int fr = lane & 15, fq = lane >> 4;
+  auto phase = [&](auto pc) {
+    constexpr int p = decltype(pc)::value;
+    wait_vm<(NPH - 1 - p) * LOADS>();  // this wave's loads of phase p have landed
+    __builtin_amdgcn_s_barrier();       // and every other wave's
+    const char* ph = smem + p * PH;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int c = ks * 4 + fq;
+      M_::frag af[TM], b0, b1;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int r = wm * (BM / 2) + 16 * i + fr;
+        af[i] = *reinterpret_cast<const bf16x8_t*>(ph + r * 128 + ((c ^ (r & 7)) << 4));
+      }
+      {
+        const int r0 = BM + wn * 32 + fr, r1 = r0 + 16;
+        b0 = *reinterpret_cast<const bf16x8_t*>(ph + r0 * 128 + ((c ^ (r0 & 7)) << 4));
+        b1 = *reinterpret_cast<const bf16x8_t*>(ph + r1 * 128 + ((c ^ (r1 & 7)) << 4));
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        acc[i][0] = M_::mma(af[i], b0, acc[i][0]);
+        acc[i][1] = M_::mma(af[i], b1, acc[i][1]);
+      }
+    }
+  };
+  for_each_index(phase, std::make_integer_sequence<int, NPH>{});
+  __syncthreads();  // every wave is done with the slice: the tile is staged over it
+  float* cs = reinterpret_cast<float*>(smem);
+  stage_tile<EPI, 64, TM, 2>(g, acc, cs, n0, wm * (BM / 2), wn * 32, lane);
+  __syncthreads();
+  store_tile<EPI, OutT, BM, 64>(g, cs, m0, n0, split, tid);
+}
+
 // ------------------------------------------------- split-K reduce + epilogue
 // v = sum_s part[s][m][n] (in split order) + bias[n], then the epilogue.
 template <typename OutT, int EPI>
@@ -553,9 +642,21 @@ static thread_local double g_flops = 0, g_bytes = 0;
 // 64-row tiles, or 32-row tiles when 64-row ones would leave more than half
 // of the 256 CUs idle (the tile height does not change any result: every
 // output element accumulates the same K slice in the same order).
+#ifndef SF_SLICE_DMA
+#define SF_SLICE_DMA 1
+#endif
 template <typename T, typename OutT, int EPI, int KS>
 static void slice_launch(const GemmArgs& g, int ns, hipStream_t s) {
   const int tiles64 = g.N / 64 * ((g.M + 63) / 64) * ns;
+  if constexpr (sizeof(T) == 2 && KS % 64 == 0 && SF_SLICE_DMA) {
+    if (tiles64 < 128)
+      klaunch(PROF_GEMM, g_flops, g_bytes, gemm_slice_dma_kernel<OutT, EPI, KS, 32>,
+              dim3(g.N / 64, (g.M + 31) / 32, ns), dim3(256), s, g);
+    else
+      klaunch(PROF_GEMM, g_flops, g_bytes, gemm_slice_dma_kernel<OutT, EPI, KS, 64>,
+              dim3(g.N / 64, (g.M + 63) / 64, ns), dim3(256), s, g);
+    return;
+  }
   if (tiles64 < 128) {
     dim3 grid(g.N / 64, (g.M + 31) / 32, ns);
     klaunch(PROF_GEMM, g_flops, g_bytes, gemm_slice_kernel<T, OutT, EPI, KS, 32>, grid, dim3(256),
