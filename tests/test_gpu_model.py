@@ -128,6 +128,23 @@ def test_encode_window_bf16_full_size(sfbf, wbf):
     assert err <= 2e-2 and agree >= 0.995
 
 
+def test_encode_window_bf16_batched_throughput_regime(sfbf, wbf):
+    """11 padded windows of 390 frames (4290 rows: the batched GEMM and
+    attention forms), 333 valid frames each: valid rows match the oracle per
+    stream and rows past n_valid do not change them."""
+    B, W, nv = 11, 390, 333
+    full = OR.pre_encode_all(make_weights("sortformer", 0, bf16=True),
+                             OF.log_mel(workload_audio("low60s")))
+    xs = np.stack([full[17 * b:17 * b + W] for b in range(B)])
+    xs[:, nv:] = np.random.default_rng(5).standard_normal((B, W - nv, 512))  # padding garbage
+    got = sfbf.encode_window(_cuda(xs), n_valid=nv).cpu().numpy()
+    for b in (0, 6, 10):
+        ref = OS.encode_window(wbf, xs[b], n_valid=nv)
+        err, agree = _report(f"window bf16 batched B={B} W={W} valid={nv} b={b}", got[b, :nv],
+                             ref[:nv])
+        assert err <= 2e-2 and agree >= 0.995
+
+
 def test_nemotron_window_fp32_and_bf16(rt, emb20):
     m = rt.Model("nemotron", "f32", seed=1)
     w = make_weights("nemotron", 1)
