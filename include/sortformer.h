@@ -241,6 +241,48 @@ sf_status sortformer_pre_encode(sf_model* model, const float* d_audio, int32_t b
                                 int64_t n_samples, float* d_mel, float* d_emb,
                                 void* d_workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------ segments */
+
+/* Speaker-activity probabilities -> speech segments. The pages give the
+ * output of diarization as [begin_seconds, end_seconds, speaker_index]
+ * segments obtained by VAD-style thresholding and smoothing of the sigmoid
+ * probabilities ("Streaming Sortformer Diarizer" model card, Output; NeMo API
+ * docs, diarize() Returns; Transformers docs, extract_speaker_dict). The
+ * parameters and their order are not printed there; per (stream, speaker)
+ * track this library applies, in order:
+ *  1. hysteresis in fp32: on when p > onset, off when p <= offset, else the
+ *     previous frame's state (off before the first frame); onset >= offset;
+ *  2. each maximal run of "on" frames [f0, f1) -> [f0*frame_s, f1*frame_s];
+ *  3. start -= pad_onset, end += pad_offset, clipped to [0, T*frame_s];
+ *  4. a segment whose gap to the previous one is below min_duration_off is
+ *     merged into it (overlaps always merge);
+ *  5. segments shorter than min_duration_on are dropped.
+ * Times are computed in fp64. Defaults: onset = offset = 0.5, everything else
+ * 0 (the segments are then exactly the runs of frames with p > 0.5). */
+typedef struct sf_segment_params {
+  float onset, offset;
+  double pad_onset, pad_offset;
+  double min_duration_on, min_duration_off;
+} sf_segment_params;
+
+typedef struct sf_segment {
+  double start_s, end_s;
+  int32_t speaker, stream;
+} sf_segment;
+
+void sortformer_segment_defaults(sf_segment_params* out);
+/* Most segments one track can hold: (T + 1) / 2. */
+int64_t sortformer_segments_capacity(int64_t n_frames);
+/* d_probs (B, T, S) fp32 on the device (S <= 64, frame_s > 0). Writes track
+ * (b, s)'s segments in time order to d_out[(b*S + s)*capacity ...] and their
+ * number to d_counts[b*S + s] (int64). capacity must be at least
+ * sortformer_segments_capacity(T) (SF_ENOMEM otherwise); params NULL = the
+ * defaults; invalid parameters -> SF_EINVAL. */
+sf_status sortformer_segments(const float* d_probs, int32_t batch, int64_t n_frames,
+                              int32_t n_spk, double frame_s, const sf_segment_params* params,
+                              sf_segment* d_out, int64_t capacity, int64_t* d_counts,
+                              void* stream);
+
 /* --------------------------------------------------------------- profiling */
 
 /* Benchmark aid: while a kernel class is profiled, every launch of that

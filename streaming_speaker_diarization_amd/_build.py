@@ -2,8 +2,8 @@
 
 Each source is compiled to an object under _build/ (in parallel), then linked
 into ``streaming_speaker_diarization_amd/libsortformer.so``. The cache
-compression unit is compiled with floating-point contraction disabled so its
-float64 key arithmetic is plain IEEE multiply/divide.
+compression and segment units are compiled with floating-point contraction
+disabled so their float64 arithmetic is plain IEEE multiply/divide/add.
 """
 from __future__ import annotations
 
@@ -20,9 +20,10 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsortformer.so")
 ARCH = os.environ.get("SF_OFFLOAD_ARCH", "gfx950")
 
-HIP_SOURCES = ["gemm.hip", "attn.hip", "misc.hip", "cache.hip", "model.hip", "api.hip", "prof.hip"]
+HIP_SOURCES = ["gemm.hip", "attn.hip", "misc.hip", "cache.hip", "segments.hip", "model.hip",
+               "api.hip", "prof.hip"]
 CPP_SOURCES = ["weights.cpp"]
-PER_FILE_FLAGS = {"cache.hip": ["-ffp-contract=off"]}
+PER_FILE_FLAGS = {"cache.hip": ["-ffp-contract=off"], "segments.hip": ["-ffp-contract=off"]}
 
 
 def _hipcc() -> str:

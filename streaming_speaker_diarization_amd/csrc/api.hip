@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
+#include <cmath>
 #include <cstring>
 #include <new>
 
@@ -597,6 +599,38 @@ sf_status sortformer_profile_end(double* ms, int64_t* launches, double* flops, d
   const int r = prof_stop(ms, &n, flops, bytes);
   if (launches) *launches = n;
   return r == 0 ? SF_OK : (r == -5 ? SF_ESTATE : SF_EHIP);
+}
+
+// ------------------------------------------------------------------ segments
+void sortformer_segment_defaults(sf_segment_params* out) {
+  if (out) *out = sf_segment_params{0.5f, 0.5f, 0.0, 0.0, 0.0, 0.0};
+}
+
+int64_t sortformer_segments_capacity(int64_t n_frames) {
+  return n_frames < 0 ? 0 : (n_frames + 1) / 2;
+}
+
+sf_status sortformer_segments(const float* d_probs, int32_t batch, int64_t n_frames,
+                              int32_t n_spk, double frame_s, const sf_segment_params* params,
+                              sf_segment* d_out, int64_t capacity, int64_t* d_counts,
+                              void* stream) {
+  if (!d_probs || !d_out || !d_counts || batch < 1 || n_frames < 0 || n_spk < 1 || n_spk > 64 ||
+      !(frame_s > 0.0) || !std::isfinite(frame_s))
+    return SF_EINVAL;
+  if (n_frames > (int64_t)INT32_MAX || (int64_t)batch * n_spk > (int64_t)INT32_MAX) return SF_ESHAPE;
+  sf_segment_params p;
+  sortformer_segment_defaults(&p);
+  if (params) p = *params;
+  const bool ok = std::isfinite(p.onset) && std::isfinite(p.offset) && p.onset >= p.offset &&
+                  p.pad_onset >= 0.0 && p.pad_offset >= 0.0 && p.min_duration_on >= 0.0 &&
+                  p.min_duration_off >= 0.0 && std::isfinite(p.pad_onset) &&
+                  std::isfinite(p.pad_offset) && std::isfinite(p.min_duration_on) &&
+                  std::isfinite(p.min_duration_off);
+  if (!ok) return SF_EINVAL;
+  if (capacity < sortformer_segments_capacity(n_frames)) return SF_ENOMEM;
+  sf::segments(d_probs, batch, (int)n_frames, n_spk, frame_s, p, d_out, capacity,
+               reinterpret_cast<long long*>(d_counts), HS(stream));
+  return launched();
 }
 
 }  // extern "C"

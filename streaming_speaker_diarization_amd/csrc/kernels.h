@@ -4,6 +4,7 @@
 #include <hip/hip_ext.h>
 
 #include "common.h"
+#include "sortformer.h"
 
 namespace sf {
 
@@ -102,6 +103,10 @@ void silence_update(const float* E, const float* P, int cap, int D, int S, int B
 void compress_cache(const float* E, const float* P, const int* ph, int cap, int D, int S, int B,
                     int M, int tail, const double* sil_sum, const int* sil_cnt, int C, int per,
                     int k, float* E2, float* P2, int* ph2, int* slots, hipStream_t s);
+
+// Probabilities (B, T, S) -> per-track segments (see segments.hip).
+void segments(const float* probs, int B, int T, int S, double dt, const sf_segment_params& prm,
+              sf_segment* out, long long cap, long long* counts, hipStream_t s);
 
 // Benchmark profiling (see prof.hip). Classes match SF_PROF_* in the ABI.
 enum { PROF_GEMM = 1, PROF_ATTN = 2, PROF_LN = 3, PROF_CONV = 4, PROF_FRONTEND = 5, PROF_CACHE = 6 };

@@ -123,3 +123,43 @@ class Stream:
             outs.append(self.step(audio[:, pos:pos + need]).clone())
             pos += need
         return torch.cat(outs, dim=1)
+
+
+# numpy view of the library's sf_segment records
+SEGMENT_DTYPE = [("start_s", "<f8"), ("end_s", "<f8"), ("speaker", "<i4"), ("stream", "<i4")]
+
+
+def segments(probs: torch.Tensor, frame_s: float = 0.08, **params):
+    """Per-frame speaker probabilities (B, T, S) on the device -> for each
+    stream a list of [start_s, end_s, speaker] segments sorted by start time
+    (then speaker). The thresholding and smoothing run in the library's
+    kernel; this only formats its per-track lists. Keyword parameters:
+    onset, offset, pad_onset, pad_offset, min_duration_on, min_duration_off."""
+    import numpy as np
+    prm = sf.sortformer_segment_defaults()
+    for k, v in params.items():
+        if not hasattr(prm, k):
+            raise TypeError(f"unknown segment parameter {k}")
+        setattr(prm, k, v)
+    probs = probs.contiguous()
+    B, T, S = probs.shape
+    if T == 0:
+        return [[] for _ in range(B)]
+    cap = sf.sortformer_segments_capacity(T)
+    out = _bytes(B * S * cap * sf.SEGMENT_BYTES, probs.device)
+    counts = torch.empty(B * S, dtype=torch.int64, device=probs.device)
+    sf.sortformer_segments(probs, frame_s, prm, out, cap, counts)
+    recs = out[:B * S * cap * sf.SEGMENT_BYTES].cpu().numpy().view(SEGMENT_DTYPE).reshape(B * S, cap)
+    n = counts.cpu().numpy()
+    result = []
+    for b in range(B):
+        segs = [[float(r["start_s"]), float(r["end_s"]), int(r["speaker"])]
+                for s in range(S) for r in recs[b * S + s, :n[b * S + s]]]
+        result.append(sorted(segs, key=lambda x: (x[0], x[2], x[1])))
+    return result
+
+
+def speaker_dicts(probs: torch.Tensor, frame_s: float = 0.08, **params):
+    """The same segments as {"Start", "End", "Speaker"} dictionaries."""
+    return [[{"Start": a, "End": e, "Speaker": k} for a, e, k in segs]
+            for segs in segments(probs, frame_s, **params)]

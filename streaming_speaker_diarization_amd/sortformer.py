@@ -31,7 +31,8 @@ EXPORTS = [
     "sortformer_encode_workspace_bytes", "sortformer_encode_window", "sortformer_pre_encode",
     "sortformer_pre_encode_workspace_bytes", "sortformer_config_num_tensors",
     "sortformer_config_tensor", "sortformer_profile_begin", "sortformer_profile_end",
-    "sortformer_stream_set_option",
+    "sortformer_stream_set_option", "sortformer_segment_defaults", "sortformer_segments_capacity",
+    "sortformer_segments",
 ]
 SF_STREAM_OPT_GRAPHS = 1
 SF_PROF = {"gemm": 1, "attn": 2, "ln": 3, "conv": 4, "frontend": 5, "cache": 6}
@@ -46,6 +47,20 @@ class sf_stream_config(C.Structure):
     _fields_ = [("chunk_len", C.c_int32), ("right_context", C.c_int32),
                 ("fifo_len", C.c_int32), ("update_period", C.c_int32),
                 ("spkcache_len", C.c_int32), ("n_sil_per_spk", C.c_int32)]
+
+
+class sf_segment_params(C.Structure):
+    _fields_ = [("onset", C.c_float), ("offset", C.c_float), ("pad_onset", C.c_double),
+                ("pad_offset", C.c_double), ("min_duration_on", C.c_double),
+                ("min_duration_off", C.c_double)]
+
+
+class sf_segment(C.Structure):
+    _fields_ = [("start_s", C.c_double), ("end_s", C.c_double), ("speaker", C.c_int32),
+                ("stream", C.c_int32)]
+
+
+SEGMENT_BYTES = C.sizeof(sf_segment)  # 24
 
 
 class SortformerError(RuntimeError):
@@ -99,6 +114,10 @@ def load(path: str = LIB_PATH):
         "sortformer_config_tensor": (I32, [cfgp, U64, I32, C.c_char_p, I32, C.POINTER(I64), P]),
         "sortformer_profile_begin": (I32, [I32, I32]),
         "sortformer_stream_set_option": (I32, [P, I32, I32]),
+        "sortformer_segment_defaults": (None, [C.POINTER(sf_segment_params)]),
+        "sortformer_segments_capacity": (I64, [I64]),
+        "sortformer_segments": (I32, [P, I32, I64, I32, C.c_double, C.POINTER(sf_segment_params),
+                                      P, I64, P, P]),
         "sortformer_profile_end": (I32, [C.POINTER(C.c_double), C.POINTER(I64),
                                          C.POINTER(C.c_double), C.POINTER(C.c_double)]),
     }
@@ -380,3 +399,30 @@ def sortformer_profile_end():
     _check(load().sortformer_profile_end(C.byref(ms), C.byref(n), C.byref(fl), C.byref(by)),
            "profile_end")
     return dict(ms=ms.value, launches=n.value, flops=fl.value, bytes=by.value)
+
+
+def sortformer_segment_defaults() -> sf_segment_params:
+    p = sf_segment_params()
+    load().sortformer_segment_defaults(C.byref(p))
+    return p
+
+
+def sortformer_segments_capacity(n_frames) -> int:
+    return load().sortformer_segments_capacity(n_frames)
+
+
+def sortformer_segments(d_probs, frame_s, params, d_out, capacity, d_counts, stream=None):
+    """d_probs (B, T, S) float32 device tensor; d_out a device byte buffer of
+    B*S*capacity segments (SEGMENT_BYTES each); d_counts int64 (B*S,)."""
+    import torch
+    B, T, S = d_probs.shape
+    out_ptr, out_bytes = _buf(d_out)
+    if out_bytes < B * S * capacity * SEGMENT_BYTES:
+        raise ValueError("segment buffer smaller than batch x speakers x capacity")
+    if not (d_counts.is_cuda and d_counts.dtype == torch.int64 and d_counts.is_contiguous()
+            and d_counts.numel() >= B * S):
+        raise TypeError("counts must be a contiguous int64 device tensor of batch x speakers")
+    _check(load().sortformer_segments(_ptr(d_probs), B, T, S, frame_s,
+                                      None if params is None else C.byref(params), out_ptr,
+                                      capacity, C.c_void_p(d_counts.data_ptr()), _stream(stream)),
+           "segments")

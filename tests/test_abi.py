@@ -112,3 +112,11 @@ def test_binding_rejects_host_strided_or_mistyped_tensors():
     with pytest.raises(TypeError):
         sortformer._buf(torch.zeros(4, dtype=torch.uint8))
     assert sortformer._ptr(None) is None
+
+
+def test_segment_defaults_and_capacity(sf):
+    p = sf.sortformer_segment_defaults()
+    assert (p.onset, p.offset, p.pad_onset, p.pad_offset, p.min_duration_on,
+            p.min_duration_off) == (0.5, 0.5, 0.0, 0.0, 0.0, 0.0)
+    assert [sf.sortformer_segments_capacity(t) for t in (0, 1, 2, 3, 64, 65)] == [0, 1, 1, 2, 32, 33]
+    assert sf.SEGMENT_BYTES == 24
