@@ -83,9 +83,11 @@ const char* sortformer_status_string(sf_status status);
 
 /* Named presets: "very_high" 340/40/40/300/188, "high" 124/1/124/124/188,
  * "low" 6/7/188/144/188, "ultra_low" 3/1/188/144/188 (model card, Streaming
- * Configurations) and "nemotron_offline" 380/0/188/192/188 (30.4 s chunks,
- * Transformers docs "Nemotron 3 Diarization", Overview). SF_EINVAL if the
- * name is unknown. */
+ * Configurations), "very_low" 6/2/188/144/188 (the 0.64 s streaming mode of
+ * the Transformers docs "Nemotron 3 Diarization", whose chunk / look-ahead
+ * split is not given: read as Low's chunk with a 2-frame look-ahead) and
+ * "nemotron_offline" 380/0/188/192/188 (30.4 s chunks, same docs, Overview).
+ * SF_EINVAL if the name is unknown. */
 sf_status sortformer_stream_preset(const char* name, sf_stream_config* out);
 
 /* ------------------------------------------------------------------ model */

@@ -52,6 +52,10 @@ PRESETS = {
     "high": (124, 1, 124, 124, 188),
     "low": (6, 7, 188, 144, 188),
     "ultra_low": (3, 1, 188, 144, 188),
+    # 0.64 s input-buffer latency (the Transformers very_low_latency mode): the
+    # pages give only the total of 8 frames; read as the Low preset's 6-frame
+    # chunk with a 2-frame look-ahead
+    "very_low": (6, 2, 188, 144, 188),
     "nemotron_offline": (380, 0, 188, 192, 188),
 }
 

@@ -207,6 +207,7 @@ sf_status sortformer_stream_preset(const char* name, sf_stream_config* out) {
                               {"high", {124, 1, 124, 124, 188}},
                               {"low", {6, 7, 188, 144, 188}},
                               {"ultra_low", {3, 1, 188, 144, 188}},
+                              {"very_low", {6, 2, 188, 144, 188}},
                               {"nemotron_offline", {380, 0, 188, 192, 188}}};
   for (const P& p : presets)
     if (std::strcmp(p.n, name) == 0) {

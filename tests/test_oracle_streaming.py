@@ -23,6 +23,9 @@ def test_presets_and_latency():
         GOLD["transformers_streaming_modes_s"]["low_latency"]
     assert S.StreamConfig.preset("ultra_low").latency_ms() / 1000 == \
         GOLD["transformers_streaming_modes_s"]["ultra_low_latency"]
+    # the 0.64 s mode (its chunk / look-ahead split is a reading; the total is the page's)
+    assert S.StreamConfig.preset("very_low").latency_ms() / 1000 == \
+        GOLD["transformers_streaming_modes_s"]["very_low_latency"]
     assert S.StreamConfig.preset("nemotron_offline").latency_ms() / 1000 == \
         GOLD["nemotron_offline_buffer_s"]["value"]
 
