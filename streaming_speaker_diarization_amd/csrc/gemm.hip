@@ -504,7 +504,9 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs g) {
 // staging): the MFMAs of phase p run while phases p+1.. are still landing.
 // Each 64-wide phase row is 8 chunks of 16 bytes, chunk c of row r stored at
 // position c ^ (r & 7); one 1 KB DMA block holds 8 rows.
-template <typename OutT, int EPI, int KS, int BM>
+// DW: the GLU + depthwise-conv epilogue (see gemm_glu_dwconv): rows
+// m0-4 .. m0+BM-5 are computed, rows m0 .. m0+BM-9 written.
+template <typename OutT, int EPI, int KS, int BM, bool DW = false>
 __global__ __launch_bounds__(256) void gemm_slice_dma_kernel(GemmArgs g) {
   using M_ = MF<bf16_t>;
   constexpr int NPH = KS / 64;                  // K phases
@@ -516,7 +518,10 @@ __global__ __launch_bounds__(256) void gemm_slice_dma_kernel(GemmArgs g) {
   __shared__ __align__(16) char smem[AB > ST ? AB : ST];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int n0 = blockIdx.x * 64, m0 = blockIdx.y * BM, split = blockIdx.z;
+  static_assert(!DW || EPI == EPI_GLU, "fused depthwise conv epilogue");
+  constexpr int DW_OUT = BM - 8;  // rows written by the depthwise-conv epilogue
+  const int n0 = blockIdx.x * 64, m0 = blockIdx.y * (DW ? DW_OUT : BM), split = blockIdx.z;
+  const int mc = DW ? m0 - 4 : m0;  // first computed row
   const int k0 = split * KS;
   const bf16_t* A = static_cast<const bf16_t*>(g.A);
   const bf16_t* Wt = static_cast<const bf16_t*>(g.W);
@@ -530,7 +535,7 @@ __global__ __launch_bounds__(256) void gemm_slice_dma_kernel(GemmArgs g) {
     for (int j = 0; j < LOADS; ++j) {
       const int blk = wave * LOADS + j;  // A blocks first, then W blocks
       if (blk < BM / 8) {
-        const int r = min(m0 + blk * 8 + lr, g.M - 1);
+        const int r = min(max(mc + blk * 8 + lr, 0), g.M - 1);
         lds_dma16(A + (size_t)r * g.lda + kk, ph + blk * 1024);
       } else {
         const int r = n0 + (blk - BM / 8) * 8 + lr;
@@ -576,7 +581,34 @@ __global__ __launch_bounds__(256) void gemm_slice_dma_kernel(GemmArgs g) {
   float* cs = reinterpret_cast<float*>(smem);
   stage_tile<EPI, 64, TM, 2>(g, acc, cs, n0, wm * (BM / 2), wn * 32, lane);
   __syncthreads();
-  store_tile<EPI, OutT, BM, 64>(g, cs, m0, n0, split, tid);
+  if constexpr (!DW) {
+    store_tile<EPI, OutT, BM, 64>(g, cs, m0, n0, split, tid);
+  } else {
+    // out[m][ch] = swish(sc * sum_t w[ch][t] glu[m+t-4][ch] + sh) for the
+    // DW_OUT rows and 32 GLU channels of this tile; cs row i holds row mc + i,
+    // taps whose frame leaves [0, dw_nvalid) of the row's stream are zero (the
+    // same sum order as dwconv_time_kernel)
+    constexpr int LDC = 32 + 4, RPT = DW_OUT / 8;
+    const int c = tid & 31, r0 = (tid >> 5) * RPT, ch = n0 / 2 + c;
+    float w9[9];
+#pragma unroll
+    for (int t = 0; t < 9; ++t) w9[t] = g.dw_w9[ch * 9 + t];
+    const float sc = g.dw_sc[ch], sh = g.dw_sh[ch];
+    int fr = (m0 + r0) % g.dw_W;
+    bf16_t* out = static_cast<bf16_t*>(g.out);
+#pragma unroll
+    for (int r = r0; r < r0 + RPT; ++r) {
+      const int m = m0 + r;
+      float acc = 0.f;
+#pragma unroll
+      for (int t = 0; t < 9; ++t) {
+        const int tt = fr + t - 4;
+        acc += (tt >= 0 && tt < g.dw_nvalid) ? w9[t] * cs[(r + t) * LDC + c] : 0.f;
+      }
+      if (m < g.M) out[(size_t)m * g.ldo + ch] = f2bf(swishf_(sc * acc + sh));
+      fr = fr + 1 == g.dw_W ? 0 : fr + 1;
+    }
+  }
 }
 
 // ------------------------------------------------- split-K reduce + epilogue
@@ -756,6 +788,19 @@ void flag_launch_failure() { g_gemm_failed = true; }
 static int checked(int r) {
   if (r < 0) g_gemm_failed = true;
   return r;
+}
+
+int gemm_glu_dwconv(const GemmArgs& g, hipStream_t s) {
+  if (g.M <= 0) return 1;
+  if (g.M > SLICE_MAX_ROWS || g.K != 512 || g.N % 64 || !g.dw_w9 || g.dw_W <= 0) {
+    g_gemm_failed = true;
+    return -1;
+  }
+  g_flops = 2.0 * g.M * g.N * g.K + 2.0 * 9 * g.M * (g.N / 2);
+  g_bytes = 2.0 * g.M * g.K + 2.0 * g.N * g.K + 2.0 * g.M * (g.N / 2);
+  klaunch(PROF_GEMM, g_flops, g_bytes, gemm_slice_dma_kernel<bf16_t, EPI_GLU, 512, 32, true>,
+          dim3(g.N / 64, (g.M + 23) / 24, 1), dim3(256), s, g);
+  return 1;
 }
 
 int gemm(const GemmArgs& g, int epi, bool bf16_in, bool bf16_out, hipStream_t s) {

@@ -31,10 +31,22 @@ struct GemmArgs {
   // EPI_QKV: columns >= vcol (the V block) go to vt transposed per head,
   // vt[((b*H + h)*hd + d)*vpitch + w] for row m = b*vrows + w.
   void* vt; int vcol, vrows, vpitch, vhd;
+  // gemm_glu_dwconv only: depthwise conv (k = 9) weights [512][9], folded
+  // BatchNorm scale / shift, and the stream layout of the rows (m = b*dw_W +
+  // frame; frames at or past dw_nvalid count as zero).
+  const float* dw_w9; const float* dw_sc; const float* dw_sh;
+  int dw_W, dw_nvalid;
 };
 // EPI_PARTIAL writes fp32 partial sums (no bias) to out as [slice][M][N] and
 // returns the slice count; other epilogues return 1.
 int gemm(const GemmArgs& g, int epi, bool bf16_in, bool bf16_out, hipStream_t s);
+// Pointwise-1 of the conformer convolution module (bf16, N = 1024 GLU
+// interleaved, K = 512) with the GLU, the depthwise conv (k = 9), the folded
+// BatchNorm and the Swish fused into its epilogue: out (M, 512) bf16. Each
+// workgroup computes 4 halo rows on either side of its 24 output rows, so the
+// convolution needs nothing from other workgroups. Windows of up to 4096 rows;
+// returns 1, or -1 (nothing launched) for other shapes.
+int gemm_glu_dwconv(const GemmArgs& g, hipStream_t s);
 // True (and cleared) if a gemm() call since the last check launched nothing
 // because its partial-sum scratch was missing or too small.
 bool take_gemm_failure();

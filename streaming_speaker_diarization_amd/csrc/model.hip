@@ -591,9 +591,20 @@ static void encode_sortformer(const sf_model* m, EncWs& w, int B, int W, int n_v
     ns = c.branch(w.ctx, 512, L.wo, 512, 512);
     c.ln(512, ns, L.bo, 1.f, L.conv_g, L.conv_b, nullptr, nullptr, 1, w.h);
     // convolution module
-    c.lin(w.h, 512, L.pw1, L.pw1_b, 1024, 512, w.glu, 512, EPI_GLU, false);
-    dwconv_time(w.glu, B, W, n_valid, L.dw9, L.dw_sc, L.dw_sh, w.h, bf, s);
-    ns = c.branch(w.h, 512, L.pw2, 512, 512);
+    if (bf && B * W <= SLICE_MAX_ROWS) {
+      // pointwise-1, GLU, depthwise conv, BatchNorm and Swish in one kernel
+      // (into ctx: h is its input)
+      GemmArgs g{};
+      g.A = w.h; g.lda = 512; g.W = L.pw1; g.ldw = 512; g.bias = L.pw1_b;
+      g.M = B * W; g.N = 1024; g.K = 512; g.out = w.ctx; g.ldo = 512;
+      g.dw_w9 = L.dw9; g.dw_sc = L.dw_sc; g.dw_sh = L.dw_sh; g.dw_W = W; g.dw_nvalid = n_valid;
+      gemm_glu_dwconv(g, s);
+      ns = c.branch(w.ctx, 512, L.pw2, 512, 512);
+    } else {
+      c.lin(w.h, 512, L.pw1, L.pw1_b, 1024, 512, w.glu, 512, EPI_GLU, false);
+      dwconv_time(w.glu, B, W, n_valid, L.dw9, L.dw_sc, L.dw_sh, w.h, bf, s);
+      ns = c.branch(w.h, 512, L.pw2, 512, 512);
+    }
     c.ln(512, ns, L.pw2_b, 1.f, L.ff2_g, L.ff2_b, nullptr, nullptr, 1, w.h);
     // macaron FFN, second half, then the output LayerNorm (fused with the
     // next layer's first LayerNorm)
