@@ -20,8 +20,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsortformer.so")
 ARCH = os.environ.get("SF_OFFLOAD_ARCH", "gfx950")
 
-HIP_SOURCES = ["gemm.hip", "attn.hip", "misc.hip", "cache.hip", "segments.hip", "model.hip",
-               "api.hip", "prof.hip"]
+HIP_SOURCES = ["gemm.hip", "attn.hip", "misc.hip", "cache.hip", "segments.hip", "tftail.hip",
+               "model.hip", "api.hip", "prof.hip"]
 CPP_SOURCES = ["weights.cpp"]
 PER_FILE_FLAGS = {"cache.hip": ["-ffp-contract=off"], "segments.hip": ["-ffp-contract=off"]}
 

@@ -74,12 +74,25 @@ void attention(const AttnArgs& a, int mode, int head_dim, bool bf16, hipStream_t
 // else LN1(v) (GEMM operand type), when non-null.
 struct LnArgs {
   float* x; int M; int D;
+  const float* x_in;  // residual read from here instead of x when non-null
   const float* part; int nsplit; const float* pbias; float alpha;
   const float *g1, *b1, *g2, *b2;
   int x_mode;
   void* y_act;
 };
 void layernorm(const LnArgs& a, bool bf16, hipStream_t s);
+
+// Post-LN transformer layer tail (d = 192, FFN 768), bf16, up to 4096 rows:
+// x1 = LN1(x + ctx Wo^T + bo) written to x1 (fp32), and the FFN's output
+// projection as 4 fp32 partial sums over hidden chunks, part[c][M][192]
+// (bias b2 not included), for a LayerNorm with x_in = x1. Returns 4.
+struct TfTailArgs {
+  const void* ctx; const float* x; float* x1; int M;
+  const void* wo; const float* bo; const float* g1; const float* be1;
+  const void* w1; const float* b1; const void* w2;
+  float* part;
+};
+int tf_tail(const TfTailArgs& a, hipStream_t s);
 
 void dwconv_time(const float* glu, int B, int W, int n_valid, const float* w9,
                  const float* scale, const float* shift, void* out, bool bf16, hipStream_t s);

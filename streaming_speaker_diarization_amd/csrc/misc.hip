@@ -17,10 +17,11 @@ __global__ __launch_bounds__(256) void ln_kernel(LnArgs a) {
   if (row >= a.M) return;
   float v[PER];
   float* xr = a.x + (size_t)row * D;
+  const float* xin = (a.x_in ? a.x_in : a.x) + (size_t)row * D;
   // every load of the row (residual + NS partial slices) is issued before use
   float pp[NS > 0 ? NS : 1][PER];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) v[i] = xr[lane + 64 * i];
+  for (int i = 0; i < PER; ++i) v[i] = xin[lane + 64 * i];
 #pragma unroll
   for (int sp = 0; sp < NS; ++sp)
 #pragma unroll

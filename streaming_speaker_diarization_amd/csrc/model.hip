@@ -627,11 +627,26 @@ static void encode_sortformer(const sf_model* m, EncWs& w, int B, int W, int n_v
     a.B = B; a.H = 8; a.W = W; a.n_valid = n_valid;
     a.ctx = w.ctx; a.ldc = 192; a.scale = 1.0f / std::sqrt(24.0f);
     attention(a, ATT_PLAIN, 24, bf, s);
-    int ns = c.branch(w.ctx, 192, L.wo, 192, 192);
-    c.ln(192, ns, L.bo, 1.f, L.ln1_g, L.ln1_b, nullptr, nullptr, 2, w.h);   // post-LN
-    c.lin(w.h, 192, L.w1, L.b1, 768, 192, w.big, 768, EPI_RELU, bf);
-    ns = c.branch(w.big, 768, L.w2, 192, 768);
-    c.ln(192, ns, L.b2, 1.f, L.ln2_g, L.ln2_b, nullptr, nullptr, 2, w.h);
+    if (bf && B * W <= SLICE_MAX_ROWS) {
+      // output projection, LN1 and the FFN's two Linears in one kernel (x1 kept
+      // in the fp32 GLU buffer, which the transformer does not otherwise use)
+      TfTailArgs t{};
+      t.ctx = w.ctx; t.x = w.x; t.x1 = w.glu; t.M = B * W;
+      t.wo = L.wo; t.bo = L.bo; t.g1 = L.ln1_g; t.be1 = L.ln1_b;
+      t.w1 = L.w1; t.b1 = L.b1; t.w2 = L.w2; t.part = w.part;
+      const int nc = tf_tail(t, s);
+      LnArgs n{};
+      n.x = w.x; n.x_in = w.glu; n.M = B * W; n.D = 192;
+      n.part = w.part; n.nsplit = nc; n.pbias = L.b2; n.alpha = 1.f;
+      n.g1 = L.ln2_g; n.b1 = L.ln2_b; n.x_mode = 2; n.y_act = w.h;
+      layernorm(n, bf, s);
+    } else {
+      int ns = c.branch(w.ctx, 192, L.wo, 192, 192);
+      c.ln(192, ns, L.bo, 1.f, L.ln1_g, L.ln1_b, nullptr, nullptr, 2, w.h);   // post-LN
+      c.lin(w.h, 192, L.w1, L.b1, 768, 192, w.big, 768, EPI_RELU, bf);
+      ns = c.branch(w.big, 768, L.w2, 192, 768);
+      c.ln(192, ns, L.b2, 1.f, L.ln2_g, L.ln2_b, nullptr, nullptr, 2, w.h);
+    }
     hin = w.h;
   }
   head_sortformer(w.x, B * W, m->h_w1t, m->h_b1, m->h_w2, m->h_b2, m->cfg.n_spk, w.probs, s);
