@@ -234,6 +234,34 @@ sf_status sortformer_encode_window(sf_model* model, const float* d_emb, int32_t 
                                    float* d_probs10, void* d_workspace, size_t workspace_bytes,
                                    void* stream);
 
+/* Test hook — per-layer taps for sortformer_encode_window ("Streaming
+ * Sortformer Diarizer" model card, Pipeline: the FastConformer and
+ * Transformer layers; Nemotron card summary: the RoPE layers). While a tap
+ * (layer, point) is registered, every sortformer_encode_window call on the
+ * model also writes that activation, widened to fp32, as (B, W, d)
+ * row-major into d_out, for all W rows (rows >= n_valid hold whatever the
+ * padded computation produced). Layers: SORTFORMER 0..16 are the conformer
+ * layers (d 512) and 17..34 the transformer layers (d 192); NEMOTRON 0..30
+ * (d 512). d_out is a device buffer of out_floats floats owned by the
+ * caller, which must keep it alive while the tap is registered; an
+ * encode_window call whose taps need more than out_floats returns SF_ENOMEM
+ * and enqueues nothing. d_out NULL removes the (layer, point) tap; layer -1
+ * with d_out NULL removes all. At most SF_MAX_TAPS taps; registering an
+ * existing (layer, point) replaces its buffer. Not thread-safe with calls on
+ * the same model; the offline and streaming calls ignore taps.
+ * Returns SF_EINVAL (null model, bad point, too many taps) or SF_ESHAPE
+ * (layer out of range). */
+#define SF_TAP_LAYER_IN 0  /* residual stream entering the layer, fp32              */
+#define SF_TAP_ATTN_CTX 1  /* attention context of all heads before W_o (compute    */
+                           /* dtype, widened)                                       */
+#define SF_TAP_LAYER_OUT 2 /* layer output as the next stage reads it: the fp32     */
+                           /* residual stream, except conformer layer 16 (the       */
+                           /* compute-dtype LN_out output fed to encoder_proj) and  */
+                           /* NEMOTRON layer 30 (after the final LayerNorm)         */
+#define SF_MAX_TAPS 16
+sf_status sortformer_debug_tap(sf_model* model, int32_t layer, int32_t point, float* d_out,
+                               size_t out_floats);
+
 /* Test hook — frontend and pre_encode alone: d_audio (B, N) -> d_mel (B, T,
  * 128) with T = floor(N/160), and -> d_emb (B, ceil(T/8), 512). Either
  * output may be NULL. Workspace: sortformer_pre_encode_workspace_bytes. */

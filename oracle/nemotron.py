@@ -54,7 +54,9 @@ def gelu(x):
     return 0.5 * x * (1.0 + erf(x / np.sqrt(2.0)))
 
 
-def rope_layer(w, l, x, n_valid):
+def rope_context(w, l, x, n_valid):
+    """Attention context (W, 512) of RoPE layer l before the output
+    projection, given the residual stream x entering the layer."""
     p = f"rl{l}."
     W = x.shape[0]
     dk = D // N_HEADS
@@ -65,8 +67,12 @@ def rope_layer(w, l, x, n_valid):
     pos = np.arange(W)
     q, k = rope(q, pos), rope(k, pos)
     a = softmax_masked(q @ k.transpose(0, 2, 1) / np.sqrt(dk), n_valid)
-    ctx = (a @ v).transpose(1, 0, 2).reshape(W, D)
-    x = x + linear(ctx, w[p + "wo"], w[p + "bo"])
+    return (a @ v).transpose(1, 0, 2).reshape(W, D)
+
+
+def rope_layer(w, l, x, n_valid):
+    p = f"rl{l}."
+    x = x + linear(rope_context(w, l, x, n_valid), w[p + "wo"], w[p + "bo"])
     h = layer_norm(x, w[p + "ln2.g"], w[p + "ln2.b"])
     return x + linear(gelu(linear(h, w[p + "w1"], w[p + "b1"])), w[p + "w2"], w[p + "b2"])
 

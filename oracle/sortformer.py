@@ -152,11 +152,12 @@ def rel_pos_table(W: int, d: int = D_FC):
     return pe
 
 
-def rel_pos_mhsa(w, p, h, n_valid):
-    """Relative-position multi-head self-attention with u/v biases.
+def rel_pos_context(w, p, h, n_valid):
+    """Relative-position multi-head attention context with u/v biases, all
+    heads concatenated (W, 512), before the output projection.
 
     score(i,j) = [(q_i+u).k_j + (q_i+v).p(i-j)] / sqrt(64), softmax over the
-    n_valid real keys, context . V, output projection.
+    n_valid real keys, times V.
     """
     W = h.shape[0]
     H, dk = N_HEADS, D_FC // N_HEADS
@@ -173,8 +174,12 @@ def rel_pos_mhsa(w, p, h, n_valid):
     j = np.arange(W)[None, :]
     bd = g[:, i, i - j + W - 1]                                     # (q_i+v).p(i-j)
     a = softmax_masked((ac + bd) / np.sqrt(dk), n_valid)
-    ctx = (a @ v).transpose(1, 0, 2).reshape(W, D_FC)
-    return linear(ctx, w[p + "att.wo"], w[p + "att.bo"])
+    return (a @ v).transpose(1, 0, 2).reshape(W, D_FC)
+
+
+def rel_pos_mhsa(w, p, h, n_valid):
+    """Relative-position self-attention: the context above, output projection."""
+    return linear(rel_pos_context(w, p, h, n_valid), w[p + "att.wo"], w[p + "att.bo"])
 
 
 def conv_module(w, p, h, n_valid):
@@ -205,16 +210,30 @@ def conformer_layer(w, l, x, n_valid):
     return layer_norm(x, w[p + "out_ln.g"], w[p + "out_ln.b"])
 
 
+def conformer_attention_context(w, l, x, n_valid):
+    """Attention context (before W_o) of conformer layer l, given the residual
+    stream x entering the layer: the first half-step FFN, LN, then
+    rel_pos_context."""
+    p = f"conf{l}."
+    x = x + 0.5 * feed_forward(w, p + "ff1.", layer_norm(x, w[p + "ff1.ln.g"], w[p + "ff1.ln.b"]))
+    return rel_pos_context(w, p, layer_norm(x, w[p + "att.ln.g"], w[p + "att.ln.b"]), n_valid)
+
+
 # ---------------------------------------------------- transformer (a6)
-def mha(w, p, x, n_valid, n_heads=N_HEADS):
+def mha_context(w, p, x, n_valid, n_heads=N_HEADS):
+    """Softmax attention context of all heads (W, d), before the output
+    projection."""
     W, d = x.shape
     dk = d // n_heads
     q = linear(x, w[p + "wq"], w[p + "bq"]).reshape(W, n_heads, dk).transpose(1, 0, 2)
     k = linear(x, w[p + "wk"], w[p + "bk"]).reshape(W, n_heads, dk).transpose(1, 0, 2)
     v = linear(x, w[p + "wv"], w[p + "bv"]).reshape(W, n_heads, dk).transpose(1, 0, 2)
     a = softmax_masked(q @ k.transpose(0, 2, 1) / np.sqrt(dk), n_valid)
-    ctx = (a @ v).transpose(1, 0, 2).reshape(W, d)
-    return linear(ctx, w[p + "wo"], w[p + "bo"])
+    return (a @ v).transpose(1, 0, 2).reshape(W, d)
+
+
+def mha(w, p, x, n_valid, n_heads=N_HEADS):
+    return linear(mha_context(w, p, x, n_valid, n_heads), w[p + "wo"], w[p + "bo"])
 
 
 def transformer_layer(w, l, x, n_valid):

@@ -558,13 +558,40 @@ sf_status sortformer_encode_window(sf_model* m, const float* d_emb, int32_t B, i
   if (ws_bytes < enc_ws_bytes(m, B, W)) return SF_ENOMEM;
   const hipStream_t s = HS(stream);
   const int S = m->cfg.n_spk;
+  for (const auto& t : m->taps)
+    if (t.cap < (size_t)B * W * tap_width(m, t.layer)) return SF_ENOMEM;
   EncWs enc = carve_enc(m, static_cast<char*>(d_ws), B, W);
   copy_rows(d_emb, 0, 512, enc.x, 0, 512, 1, B * W, 512, s);
-  encode(m, enc, B, W, n_valid, s);
+  encode(m, enc, B, W, n_valid, s, true);
   copy_rows(enc.probs, 0, S, d_probs, 0, S, 1, B * W, S, s);
   if (d_probs10 && m->cfg.arch == SF_ARCH_NEMOTRON)
     copy_rows(enc.probs10, 0, S, d_probs10, 0, S, 1, B * W * 8, S, s);
   return launched();
+}
+
+sf_status sortformer_debug_tap(sf_model* m, int32_t layer, int32_t point, float* d_out,
+                               size_t out_floats) {
+  if (!m) return SF_EINVAL;
+  if (layer == -1 && !d_out) {
+    m->taps.clear();
+    return SF_OK;
+  }
+  if (point < SF_TAP_LAYER_IN || point > SF_TAP_LAYER_OUT) return SF_EINVAL;
+  if (layer < 0 || layer >= tap_layers(m)) return SF_ESHAPE;
+  auto it = m->taps.begin();
+  while (it != m->taps.end() && !(it->layer == layer && it->point == point)) ++it;
+  if (!d_out) {
+    if (it != m->taps.end()) m->taps.erase(it);
+    return SF_OK;
+  }
+  if (it != m->taps.end()) {
+    it->out = d_out;
+    it->cap = out_floats;
+    return SF_OK;
+  }
+  if (m->taps.size() >= SF_MAX_TAPS) return SF_EINVAL;
+  m->taps.push_back({layer, point, d_out, out_floats});
+  return SF_OK;
 }
 
 size_t sortformer_pre_encode_workspace_bytes(const sf_model* m, int32_t B, int64_t N) {

@@ -44,6 +44,11 @@ struct TfLayer {
 }  // namespace sfh
 
 struct sf_model {
+  struct Tap {
+    int layer, point;
+    float* out;
+    size_t cap;  // floats
+  };
   sf_model_config cfg;
   bool bf16;
   size_t esz;  // bytes per GEMM operand element
@@ -68,6 +73,8 @@ struct sf_model {
   const float *fin_g, *fin_b, *nh_w, *nh_b, *up_w, *up_b, *rope;
   // frontend tables
   const float* fe_tab;
+  // per-layer taps honoured by sortformer_encode_window
+  std::vector<Tap> taps;
 };
 
 struct sf_stream {

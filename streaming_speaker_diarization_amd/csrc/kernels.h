@@ -117,6 +117,8 @@ void head_nemotron(const float* x, int M, const float* hw, const float* hb, cons
 
 void copy_rows(const float* src, long long s_bstride, int s_ld, float* dst, long long d_bstride,
                int d_ld, int B, int rows, int cols, hipStream_t s);
+// n contiguous elements (fp32, or bf16 when src_bf16) widened to fp32
+void widen(const void* src, bool src_bf16, float* dst, long long n, hipStream_t s);
 void ring_write(const float* src, long long n_new, int B, float* ring, long long ring_cap,
                 long long start, hipStream_t s);
 void fill_i32(int* p, long long n, int v, hipStream_t s);

@@ -472,6 +472,18 @@ void copy_rows(const float* src, long long sb, int sl, float* dst, long long db,
                      sl, dst, db, dl, cols);
 }
 
+__global__ void widen_kernel(const void* src, bool bf, float* dst, long long n) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i < n)
+    dst[i] = bf ? bf2f(static_cast<const bf16_t*>(src)[i]) : static_cast<const float*>(src)[i];
+}
+
+void widen(const void* src, bool src_bf16, float* dst, long long n, hipStream_t s) {
+  if (n <= 0) return;
+  hipLaunchKernelGGL(widen_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src,
+                     src_bf16, dst, n);
+}
+
 __global__ void ring_write_kernel(const float* src, long long n, float* ring, long long cap,
                                   long long start) {
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;

@@ -29,6 +29,10 @@ size_t pre_ws_bytes(const sf_model* m, int B, int n);
 void pre_encode_range(const sf_model* m, const float* audio, long long a_bstride,
                       long long ring_mask, long long n_total, int T, int e0, int e1, int B,
                       float* dst, long long dst_bstride, char* wsp, hipStream_t s);
-void encode(const sf_model* m, EncWs& w, int B, int W, int n_valid, hipStream_t s);
+// taps: honour m->taps (the caller has checked their capacities)
+void encode(const sf_model* m, EncWs& w, int B, int W, int n_valid, hipStream_t s,
+            bool taps = false);
+int tap_layers(const sf_model* m);
+int tap_width(const sf_model* m, int layer);
 
 }  // namespace sfm

@@ -569,13 +569,34 @@ struct Ctx {
 };
 }  // namespace
 
+namespace {
+// Copies of registered (layer, point) activations, widened to fp32.
+struct Taps {
+  const sf_model* m;
+  bool on;
+  long long rows;
+  hipStream_t s;
+  void at(int layer, int point, const void* src, bool src_bf16, int d) const {
+    if (!on) return;
+    for (const auto& t : m->taps)
+      if (t.layer == layer && t.point == point) widen(src, src_bf16, t.out, rows * d, s);
+  }
+};
+}  // namespace
+
+int tap_layers(const sf_model* m) { return m->cfg.arch == SF_ARCH_SORTFORMER ? 35 : 31; }
+int tap_width(const sf_model* m, int layer) {
+  return m->cfg.arch == SF_ARCH_SORTFORMER && layer >= 17 ? 192 : 512;
+}
+
 static void encode_sortformer(const sf_model* m, EncWs& w, int B, int W, int n_valid,
-                              hipStream_t s) {
+                              hipStream_t s, const Taps& tp) {
   const bool bf = m->bf16;
   Ctx c{m, w, B * W, s, bf};
   c.ln(512, 0, nullptr, 0.f, m->conf[0].ff1_g, m->conf[0].ff1_b, nullptr, nullptr, 0, w.h);
   for (int l = 0; l < 17; ++l) {
     const ConfLayer& L = m->conf[l];
+    tp.at(l, SF_TAP_LAYER_IN, w.x, false, 512);
     // macaron FFN, first half: x += FF(LN(x))/2
     c.lin(w.h, 512, L.ff1_w1, L.ff1_b1, 2048, 512, w.big, 2048, EPI_SWISH, bf);
     int ns = c.branch(w.big, 2048, L.ff1_w2, 512, 2048);
@@ -588,6 +609,7 @@ static void encode_sortformer(const sf_model* m, EncWs& w, int B, int W, int n_v
     a.ub = L.u; a.vb = L.v; a.P = L.P; a.ldp = 512; a.p_center = SF_MAX_WINDOW - 1;
     a.ctx = w.ctx; a.ldc = 512; a.scale = 0.125f;
     attention(a, ATT_RELPOS, 64, bf, s);
+    tp.at(l, SF_TAP_ATTN_CTX, w.ctx, bf, 512);
     ns = c.branch(w.ctx, 512, L.wo, 512, 512);
     c.ln(512, ns, L.bo, 1.f, L.conv_g, L.conv_b, nullptr, nullptr, 1, w.h);
     // convolution module
@@ -610,23 +632,28 @@ static void encode_sortformer(const sf_model* m, EncWs& w, int B, int W, int n_v
     // next layer's first LayerNorm)
     c.lin(w.h, 512, L.ff2_w1, L.ff2_b1, 2048, 512, w.big, 2048, EPI_SWISH, bf);
     ns = c.branch(w.big, 2048, L.ff2_w2, 512, 2048);
-    if (l < 16)
+    if (l < 16) {
       c.ln(512, ns, L.ff2_b2, 0.5f, L.out_g, L.out_b, m->conf[l + 1].ff1_g, m->conf[l + 1].ff1_b,
            2, w.h);
-    else
+      tp.at(l, SF_TAP_LAYER_OUT, w.x, false, 512);
+    } else {
       c.ln(512, ns, L.ff2_b2, 0.5f, L.out_g, L.out_b, nullptr, nullptr, 0, w.h);
+      tp.at(l, SF_TAP_LAYER_OUT, w.h, bf, 512);
+    }
   }
   // encoder_proj: fp32 residual stream of the transformer + GEMM operand
   c.lin(w.h, 512, m->proj_w, m->proj_b, 192, 512, w.ctx, 192, EPI_STORE, bf, w.x, 192);
   const void* hin = w.ctx;
   for (int l = 0; l < 18; ++l) {
     const TfLayer& L = m->tf[l];
+    tp.at(17 + l, SF_TAP_LAYER_IN, w.x, false, 192);
     c.qkv(hin, 192, L.wqkv, L.bqkv, w.big, 24, W);
     AttnArgs a{};
     a.qkv = w.big; a.ldq = 576; a.qoff = 0; a.koff = 192; a.vt = w.vt; a.vpitch = w.vpitch;
     a.B = B; a.H = 8; a.W = W; a.n_valid = n_valid;
     a.ctx = w.ctx; a.ldc = 192; a.scale = 1.0f / std::sqrt(24.0f);
     attention(a, ATT_PLAIN, 24, bf, s);
+    tp.at(17 + l, SF_TAP_ATTN_CTX, w.ctx, bf, 192);
     if (bf && B * W <= SLICE_MAX_ROWS) {
       // output projection, LN1 and the FFN's two Linears in one kernel (x1 kept
       // in the fp32 GLU buffer, which the transformer does not otherwise use)
@@ -647,24 +674,27 @@ static void encode_sortformer(const sf_model* m, EncWs& w, int B, int W, int n_v
       ns = c.branch(w.big, 768, L.w2, 192, 768);
       c.ln(192, ns, L.b2, 1.f, L.ln2_g, L.ln2_b, nullptr, nullptr, 2, w.h);
     }
+    tp.at(17 + l, SF_TAP_LAYER_OUT, w.x, false, 192);
     hin = w.h;
   }
   head_sortformer(w.x, B * W, m->h_w1t, m->h_b1, m->h_w2, m->h_b2, m->cfg.n_spk, w.probs, s);
 }
 
 static void encode_nemotron(const sf_model* m, EncWs& w, int B, int W, int n_valid,
-                            hipStream_t s) {
+                            hipStream_t s, const Taps& tp) {
   const bool bf = m->bf16;
   Ctx c{m, w, B * W, s, bf};
   c.ln(512, 0, nullptr, 0.f, m->rl[0].ln1_g, m->rl[0].ln1_b, nullptr, nullptr, 0, w.h);
   for (int l = 0; l < 31; ++l) {
     const TfLayer& L = m->rl[l];
+    tp.at(l, SF_TAP_LAYER_IN, w.x, false, 512);
     c.qkv(w.h, 512, L.wqkv, L.bqkv, w.big, 64, W);
     AttnArgs a{};
     a.qkv = w.big; a.ldq = 1536; a.qoff = 0; a.koff = 512; a.vt = w.vt; a.vpitch = w.vpitch;
     a.B = B; a.H = 8; a.W = W; a.n_valid = n_valid; a.rope = m->rope;
     a.ctx = w.ctx; a.ldc = 512; a.scale = 0.125f;
     attention(a, ATT_ROPE, 64, bf, s);
+    tp.at(l, SF_TAP_ATTN_CTX, w.ctx, bf, 512);
     int ns = c.branch(w.ctx, 512, L.wo, 512, 512);
     c.ln(512, ns, L.bo, 1.f, L.ln2_g, L.ln2_b, nullptr, nullptr, 1, w.h);   // pre-LN
     c.lin(w.h, 512, L.w1, L.b1, 2048, 512, w.big, 2048, EPI_GELU, bf);
@@ -673,13 +703,15 @@ static void encode_nemotron(const sf_model* m, EncWs& w, int B, int W, int n_val
       c.ln(512, ns, L.b2, 1.f, m->rl[l + 1].ln1_g, m->rl[l + 1].ln1_b, nullptr, nullptr, 1, w.h);
     else
       c.ln(512, ns, L.b2, 1.f, m->fin_g, m->fin_b, nullptr, nullptr, 2, nullptr);  // final LN
+    tp.at(l, SF_TAP_LAYER_OUT, w.x, false, 512);
   }
   head_nemotron(w.x, B * W, m->nh_w, m->nh_b, m->up_w, m->up_b, w.probs, w.probs10, s);
 }
 
-void encode(const sf_model* m, EncWs& w, int B, int W, int n_valid, hipStream_t s) {
-  if (m->cfg.arch == SF_ARCH_SORTFORMER) encode_sortformer(m, w, B, W, n_valid, s);
-  else encode_nemotron(m, w, B, W, n_valid, s);
+void encode(const sf_model* m, EncWs& w, int B, int W, int n_valid, hipStream_t s, bool taps) {
+  const Taps tp{m, taps && !m->taps.empty(), (long long)B * W, s};
+  if (m->cfg.arch == SF_ARCH_SORTFORMER) encode_sortformer(m, w, B, W, n_valid, s, tp);
+  else encode_nemotron(m, w, B, W, n_valid, s, tp);
 }
 
 }  // namespace sfm

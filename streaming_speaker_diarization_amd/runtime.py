@@ -28,6 +28,7 @@ class Model:
         self.handle = sf.sortformer_init(self.cfg, self.seed, self.weights)
         self.n_spk = self.cfg.n_spk
         self._ws = None
+        self._taps = {}  # keeps registered tap buffers alive
 
     def __del__(self):
         h = getattr(self, "handle", None)
@@ -58,6 +59,20 @@ class Model:
         sf.sortformer_encode_window(self.handle, emb.contiguous(), W if n_valid is None else n_valid,
                                     p, p10, ws)
         return p if p10 is None else (p, p10)
+
+    def tap(self, layer: int, point: int, out: torch.Tensor | None):
+        """Have encode_window also write the (layer, point) activation into
+        `out` (float32, at least batch x window x width elements); None
+        removes the tap. The tensor must outlive the registration."""
+        sf.sortformer_debug_tap(self.handle, layer, point, out)
+        if out is None:
+            self._taps.pop((layer, point), None)
+        else:
+            self._taps[(layer, point)] = out
+
+    def clear_taps(self):
+        sf.sortformer_debug_tap(self.handle, -1, 0, None)
+        self._taps.clear()
 
     def pre_encode(self, audio: torch.Tensor):
         B, N = audio.shape

@@ -32,9 +32,11 @@ EXPORTS = [
     "sortformer_pre_encode_workspace_bytes", "sortformer_config_num_tensors",
     "sortformer_config_tensor", "sortformer_profile_begin", "sortformer_profile_end",
     "sortformer_stream_set_option", "sortformer_segment_defaults", "sortformer_segments_capacity",
-    "sortformer_segments",
+    "sortformer_segments", "sortformer_debug_tap",
 ]
 SF_STREAM_OPT_GRAPHS = 1
+SF_TAP_LAYER_IN, SF_TAP_ATTN_CTX, SF_TAP_LAYER_OUT = 0, 1, 2
+SF_MAX_TAPS = 16
 SF_PROF = {"gemm": 1, "attn": 2, "ln": 3, "conv": 4, "frontend": 5, "cache": 6}
 
 
@@ -108,6 +110,7 @@ def load(path: str = LIB_PATH):
         "sortformer_stream_update": (I32, [P, P, I32, P, SZ, P]),
         "sortformer_encode_workspace_bytes": (SZ, [P, I32, I32]),
         "sortformer_encode_window": (I32, [P, P, I32, I32, I32, P, P, P, SZ, P]),
+        "sortformer_debug_tap": (I32, [P, I32, I32, P, SZ]),
         "sortformer_pre_encode": (I32, [P, P, I32, I64, P, P, P, SZ, P]),
         "sortformer_pre_encode_workspace_bytes": (SZ, [P, I32, I64]),
         "sortformer_config_num_tensors": (I32, [cfgp]),
@@ -375,6 +378,13 @@ def sortformer_encode_window(h, d_emb, n_valid, d_probs, d_probs10, d_ws, stream
                                            _ptr(d_probs, B * W * cfg.n_spk),
                                            _ptr(d_probs10, 8 * B * W * cfg.n_spk),
                                            *_buf(d_ws), _stream(stream)), "encode_window")
+
+
+def sortformer_debug_tap(h, layer, point, d_out):
+    """Register (d_out a float32 GPU tensor) or remove (d_out None) a tap;
+    layer -1 with d_out None removes every tap."""
+    n = 0 if d_out is None else d_out.numel()
+    _check(load().sortformer_debug_tap(h, layer, point, _ptr(d_out), n), "debug_tap")
 
 
 def sortformer_pre_encode_workspace_bytes(h, batch, n_samples) -> int:
