@@ -32,12 +32,7 @@ template <> struct Pack<float> {
   __device__ static float make(const float* v) { return v[0]; }
 };
 template <> struct Pack<bf16_t> {
-  __device__ static bf16x8_t make(const float* v) {
-    u16x8 u;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) u[e] = f2bf(v[e]);
-    return __builtin_bit_cast(bf16x8_t, u);
-  }
+  __device__ static bf16x8_t make(const float* v) { return pack_bf16x8(v); }
 };
 
 // Fragment I/O: EPF consecutive elements (8 bf16 or 1 fp32) as one load.
@@ -343,64 +338,73 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------------------
 // Throughput form for batched windows (streams x window above 4096 rows),
-// bf16: one workgroup = 64 query rows (16 per wave) of one (stream, head).
-// The four waves share each 64-key tile of K, V^T and (relative positions)
-// the 128-row band of p(delta) the tile's (i, j) pairs touch, staged once in
-// LDS per tile while the next tile's loads are in flight in registers; each
-// wave runs the online softmax over all tiles for its own rows. Same
-// arithmetic per tile as the latency form above; only the order in which the
-// key tiles are combined differs.
+// bf16: one workgroup = 128 query rows (32 per wave, as two 16-row sets) of
+// one (stream, head). Each 64-key tile of K, V^T and (relative positions) the
+// 192-row band of p(delta) its (i, j) pairs touch is staged once in LDS per
+// tile while the next tile's loads are in flight in registers. The products
+// are taken transposed, S^T = K Q^T and O^T = V^T P^T: a lane then holds 16
+// scores of one query, so the softmax statistics are lane-local up to one
+// exchange across the four lane groups, and the probabilities are already
+// the B operand of the second product in registers (the 32 keys of a k-step
+// are matched to V^T by storing each 32-key block of V^T in that order).
+// The K, V^T and band fragments read from LDS serve both query sets.
 template <int HD, int MODE>
-__global__ __launch_bounds__(256) void attn_tp_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_tp_kernel(AttnArgs a) {
   using M_ = MF<bf16_t>;
   constexpr int HDP = HD <= 32 ? 32 : 64;  // head dim padded for MFMA
   constexpr int NQF = HDP / 32;            // k-steps over head dims
-  constexpr int NDT = HDP / 16;            // output column tiles
+  constexpr int NDT = HDP / 16;            // 16-dim tiles of the output
   constexpr int LK = HDP + 8;              // K / band row pitch (bf16)
   constexpr int LV = 64 + 8;               // V^T row pitch
-  constexpr int LDP = 72;
+  constexpr int GP = 20;                   // G^T row pitch (fp32), conflict-free both ways
   constexpr bool REL = MODE == ATT_RELPOS;
-  constexpr int NB = REL ? 128 : 0;        // band rows per tile
+  constexpr int QB = 128;                  // query rows per workgroup
+  constexpr int NB = REL ? QB + 64 : 0;    // band rows per key tile
   constexpr int CPK = HDP / 8;             // 16-byte chunks per K / band row
   constexpr int NCK = 64 * CPK / 256, NCV = HDP * 8 / 256, NCB = NB * CPK / 256;
   static_assert(MODE != ATT_ROPE, "rotary layers use the latency form");
   __shared__ __align__(16) bf16_t Ks[64 * LK];
   __shared__ __align__(16) bf16_t Vs[HDP * LV];
   __shared__ __align__(16) bf16_t Bs[REL ? NB * LK : 8];
-  __shared__ float Gs[REL ? 4 * 16 * 81 : 1];
-  __shared__ __align__(16) bf16_t Ps[4 * 16 * LDP];
+  __shared__ float Gs[REL ? 4 * 80 * GP : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c16 = lane & 15;
-  const int iq0 = blockIdx.x * 64, h = blockIdx.y, b = blockIdx.z;
-  const int iw = iq0 + 16 * w;  // this wave's first query row
+  const int iq0 = blockIdx.x * QB, h = blockIdx.y, b = blockIdx.z;
+  const int iw = iq0 + 32 * w;  // this wave's first query row
   const bf16_t* qkv = static_cast<const bf16_t*>(a.qkv);
   const size_t rowbase = (size_t)b * a.W;
   const float sl2 = a.scale * 1.4426950408889634f;
   const bf16_t* vtb = static_cast<const bf16_t*>(a.vt) + (size_t)(b * a.H + h) * HD * a.vpitch;
   const bf16_t* P = static_cast<const bf16_t*>(a.P);
 
-  // ---- query fragments of row iw + c16 (element e of fragment ks is dim
-  // ks*32 + 8g + e), with the u / v biases for relative positions
-  bf16x8_t qa[NQF], qb[NQF];
-  {
-    const int qi = iw + c16, qc = min(qi, a.W - 1);
+  // ---- Q^T fragments (B operand): column c16 = query iw + 16s + c16, element
+  // e of k-step ks = dim 32ks + 8g + e; qb carries the v bias for positions
+  bf16x8_t qa[2][NQF], qb[2][NQF];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int qi = iw + 16 * s + c16, qc = min(qi, a.W - 1);
 #pragma unroll
     for (int ks = 0; ks < NQF; ++ks) {
+      const int d0 = 32 * ks + 8 * g;
+      const vec16 raw = *reinterpret_cast<const vec16*>(
+          qkv + (rowbase + qc) * a.ldq + a.qoff + h * HD + min(d0, HD - 8));
+      const bool live = qi < a.W && d0 < HD;
       float ua[8], va[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int d = ks * 32 + 8 * g + e, dc = min(d, HD - 1);
-        float q = bf2f(qkv[(rowbase + qc) * a.ldq + a.qoff + h * HD + dc]);
-        q = (qi < a.W && d < HD) ? q : 0.f;
+        const uint32_t wv = raw.w[e / 2];
+        const float q = live ? __uint_as_float(e & 1 ? (wv & 0xFFFF0000u) : (wv << 16)) : 0.f;
         ua[e] = q;
         va[e] = q;
         if constexpr (REL) {
-          ua[e] += d < HD ? a.ub[h * HD + dc] : 0.f;
-          va[e] += d < HD ? a.vb[h * HD + dc] : 0.f;
+          const int dc = min(d0 + e, HD - 1);
+          ua[e] += d0 < HD ? a.ub[h * HD + dc] : 0.f;
+          va[e] += d0 < HD ? a.vb[h * HD + dc] : 0.f;
         }
       }
-      qa[ks] = Pack<bf16_t>::make(ua);
-      qb[ks] = Pack<bf16_t>::make(va);
+      qa[s][ks] = Pack<bf16_t>::make(ua);
+      qb[s][ks] = Pack<bf16_t>::make(va);
     }
   }
 
@@ -410,7 +414,7 @@ __global__ __launch_bounds__(256) void attn_tp_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < NCK; ++i) {
       const int c = tid + 256 * i, r = c / CPK, q = c % CPK;
-      const int j = min(j0 + r, a.W - 1), d = min(8 * q, (HD / 8 - 1) * 8);
+      const int j = min(j0 + r, a.W - 1), d = min(8 * q, HD - 8);
       rk[i] = *reinterpret_cast<const vec16*>(qkv + (rowbase + j) * a.ldq + a.koff + h * HD + d);
     }
 #pragma unroll
@@ -426,7 +430,10 @@ __global__ __launch_bounds__(256) void attn_tp_kernel(AttnArgs a) {
       rbd[i] = *reinterpret_cast<const vec16*>(P + (size_t)pr * a.ldp + h * HD + 8 * q);
     }
   };
-  // zero what lies outside the head, the window or the position table
+  // zero what lies outside the head, the window or the position table; V^T
+  // keys go to their k-slot order (in-block key 16u + 4v + t at 8v + 4u + t)
+  // (the masks are workgroup-uniform no-ops except on a tile that crosses
+  // the window end or a band that leaves the position table)
   auto stash = [&](int j0) {
 #pragma unroll
     for (int i = 0; i < NCK; ++i) {
@@ -436,35 +443,47 @@ __global__ __launch_bounds__(256) void attn_tp_kernel(AttnArgs a) {
       for (int e = 0; e < 4; ++e) rk[i].w[e] = live ? rk[i].w[e] : 0u;
       *reinterpret_cast<vec16*>(&Ks[r * LK + 8 * q]) = rk[i];
     }
+    const bool vedge = j0 + 64 > a.W;
 #pragma unroll
     for (int i = 0; i < NCV; ++i) {
       const int c = tid + 256 * i, d = c / 8, q = c % 8, j = j0 + 8 * q;
+      uint32_t m[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t v = d < HD ? rv[i].w[e] : 0u;
-        const uint32_t lo = j + 2 * e < a.W ? (v & 0xFFFFu) : 0u;
-        const uint32_t hi = j + 2 * e + 1 < a.W ? (v & 0xFFFF0000u) : 0u;
-        rv[i].w[e] = lo | hi;
+      for (int e = 0; e < 4; ++e) m[e] = d < HD ? rv[i].w[e] : 0u;
+      if (vedge) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t lo = j + 2 * e < a.W ? (m[e] & 0xFFFFu) : 0u;
+          const uint32_t hi = j + 2 * e + 1 < a.W ? (m[e] & 0xFFFF0000u) : 0u;
+          m[e] = lo | hi;
+        }
       }
-      *reinterpret_cast<vec16*>(&Vs[d * LV + 8 * q]) = rv[i];
+      const int qq = q & 3;
+      bf16_t* dst = &Vs[d * LV + 32 * (q >> 2) + 16 * (qq & 1) + 4 * (qq >> 1)];
+      *reinterpret_cast<uint2*>(dst) = uint2{m[0], m[1]};
+      *reinterpret_cast<uint2*>(dst + 8) = uint2{m[2], m[3]};
     }
+    const bool bedge = iq0 - j0 - 63 < -a.p_center || iq0 - j0 - 63 + NB - 1 > a.p_center;
 #pragma unroll
     for (int i = 0; i < NCB; ++i) {
       const int c = tid + 256 * i, r = c / CPK, q = c % CPK;
       const int dl = iq0 - j0 - 63 + r;
-      const bool live = dl >= -a.p_center && dl <= a.p_center && 8 * q < HD;
+      if (bedge) {
+        const bool live = dl >= -a.p_center && dl <= a.p_center;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) rbd[i].w[e] = live ? rbd[i].w[e] : 0u;
+        for (int e = 0; e < 4; ++e) rbd[i].w[e] = live ? rbd[i].w[e] : 0u;
+      }
       *reinterpret_cast<vec16*>(&Bs[r * LK + 8 * q]) = rbd[i];
     }
   };
 
-  f32x4 O[NDT];
+  // O^T: lane (g, c16) holds dims 16dt + 4g + r of query iw + 16s + c16
+  f32x4 O[2][NDT];
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float mrow[4], lrow[4];
+  for (int s = 0; s < 2; ++s)
 #pragma unroll
-  for (int r = 0; r < 4; ++r) { mrow[r] = -INFINITY; lrow[r] = 0.f; }
+    for (int dt = 0; dt < NDT; ++dt) O[s][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};  // lrow: this lane's keys
 
   const int ntile = (a.n_valid + 63) / 64;
   fetch(0);
@@ -477,88 +496,134 @@ __global__ __launch_bounds__(256) void attn_tp_kernel(AttnArgs a) {
     // staging arrays in registers), in flight while this tile is used
     fetch(min(j0 + 64, (ntile - 1) * 64));
 
-    // ---- scores
-    f32x4 S[4];
+    // ---- S^T: lane (g, c16) holds keys j0 + 16nt + 4g + r of its query
+    f32x4 S[2][4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      S[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      S[0][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      S[1][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < NQF; ++ks)
-        S[nt] = M_::mma(qa[ks], *reinterpret_cast<const bf16x8_t*>(
-                                    &Ks[(16 * nt + c16) * LK + ks * 32 + 8 * g]), S[nt]);
+      for (int ks = 0; ks < NQF; ++ks) {
+        const bf16x8_t kf =
+            *reinterpret_cast<const bf16x8_t*>(&Ks[(16 * nt + c16) * LK + ks * 32 + 8 * g]);
+        S[0][nt] = M_::mma(kf, qa[0][ks], S[0][nt]);
+        S[1][nt] = M_::mma(kf, qa[1][ks], S[1][nt]);
+      }
     }
     if constexpr (REL) {
-      // G[i][c] = (q_i+v).p(delta), band row 16w + c <-> delta iw-j0-63+c;
-      // the score of (i, j) takes column i-j+63
-      float* G = &Gs[w * 16 * 81];
+      // G^T[rho][c] = p(delta).(q_c + v) with band row 32w + 16s + rho <->
+      // delta = (iw + 16s) - j0 - 63 + rho; the score of (query c, key k)
+      // takes rho = c - k + 63
+      float* G = &Gs[w * 80 * GP];
+      bf16x8_t bfr[6][NQF];
 #pragma unroll
-      for (int ct = 0; ct < 5; ++ct) {
-        f32x4 acc{0.f, 0.f, 0.f, 0.f};
+      for (int bt = 0; bt < 6; ++bt)
 #pragma unroll
         for (int ks = 0; ks < NQF; ++ks)
-          acc = M_::mma(qb[ks], *reinterpret_cast<const bf16x8_t*>(
-                                    &Bs[(16 * w + 16 * ct + c16) * LK + ks * 32 + 8 * g]), acc);
+          bfr[bt][ks] = *reinterpret_cast<const bf16x8_t*>(
+              &Bs[(32 * w + 16 * bt + c16) * LK + ks * 32 + 8 * g]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) G[(4 * g + r) * 81 + 16 * ct + c16] = acc[r];
+      for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int ct = 0; ct < 5; ++ct) {
+          f32x4 acc{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < NQF; ++ks) acc = M_::mma(bfr[s + ct][ks], qb[s][ks], acc);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) G[(16 * ct + 4 * g + r) * GP + c16] = acc[r];
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            S[s][nt][r] += G[(c16 - 16 * nt - 4 * g - r + 63) * GP + c16];
+        wave_lds_sync();  // the next set rewrites G
       }
-      wave_lds_sync();
+    }
+
+    // ---- online softmax (log2 domain: the running max is kept scaled by
+    // scale*log2(e), p = 2^(s*scale*log2(e) - m)); P^T as the B operand of
+    // O^T += V^T P^T. Keys past n_valid exist only in the last tile.
+    if (j0 + 64 > a.n_valid) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            S[s][nt][r] = j0 + 16 * nt + 4 * g + r < a.n_valid ? S[s][nt][r] : -INFINITY;
+    }
+    bf16x8_t pb[2][2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      float mx = -INFINITY;
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          S[nt][r] += G[(4 * g + r) * 81 + (4 * g + r) - (16 * nt + c16) + 63];
-    }
-
-    // ---- online softmax (log2 domain)
-    float mx[4];
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, S[s][nt][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(mrow[s], mx * sl2);
+      float rs = 0.f, p[4][4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) mx[r] = -INFINITY;
+      for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const bool valid = j0 + 16 * nt + c16 < a.n_valid;
+        for (int r = 0; r < 4; ++r) {
+          p[nt][r] = __builtin_amdgcn_exp2f(fmaf(S[s][nt][r], sl2, -mnew));
+          rs += p[nt][r];
+        }
+      if (__ballot(mnew != mrow[s])) {  // rescale only when some query's max moved
+        const float alpha = __builtin_amdgcn_exp2f(mrow[s] - mnew);
+        lrow[s] *= alpha;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        S[nt][r] = valid ? S[nt][r] * sl2 : -INFINITY;
-        mx[r] = fmaxf(mx[r], S[nt][r]);
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) O[s][dt][r] *= alpha;
+      }
+      lrow[s] += rs;
+      mrow[s] = mnew;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pv[e] = p[2 * ks][e];
+          pv[4 + e] = p[2 * ks + 1][e];
+        }
+        pb[s][ks] = Pack<bf16_t>::make(pv);
       }
     }
-    bf16_t* Pw = &Ps[w * 16 * LDP];
+    // ---- O^T += V^T P^T (V^T columns past the window or the head are zero)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float mnew = fmaxf(mrow[r], row16_max(mx[r]));
-      const float alpha = exp2f(mrow[r] - mnew);
-      float rs = 0.f;
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const float p = exp2f(S[nt][r] - mnew);
-        rs += p;
-        Pw[(4 * g + r) * LDP + 16 * nt + c16] = f2bf(p);
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8_t vf =
+            *reinterpret_cast<const bf16x8_t*>(&Vs[(16 * dt + c16) * LV + ks * 32 + 8 * g]);
+        O[0][dt] = M_::mma(vf, pb[0][ks], O[0][dt]);
+        O[1][dt] = M_::mma(vf, pb[1][ks], O[1][dt]);
       }
-      lrow[r] = lrow[r] * alpha + row16_sum(rs);
-      mrow[r] = mnew;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) O[dt][r] *= alpha;
-    }
-    wave_lds_sync();
-    // ---- O += P.V
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const auto pa = M_::ld(&Pw[c16 * LDP + ks * 32], lane);
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-        O[dt] = M_::mma(pa, *reinterpret_cast<const bf16x8_t*>(
-                                &Vs[(16 * dt + c16) * LV + ks * 32 + 8 * g]), O[dt]);
-    }
   }
 
   bf16_t* ctx = static_cast<bf16_t*>(a.ctx);
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
+  for (int s = 0; s < 2; ++s) {
+    float l = lrow[s];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const int i = iw + 16 * s + c16;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = iw + 4 * g + r, d = 16 * dt + c16;
-      if (i < a.W && d < HD) ctx[(rowbase + i) * a.ldc + h * HD + d] = f2bf(O[dt][r] / lrow[r]);
+    for (int dt = 0; dt < NDT; ++dt) {
+      const int d = 16 * dt + 4 * g;
+      if (i < a.W && d < HD) {
+        u16x4 u;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) u[r] = f2bf(O[s][dt][r] / l);
+        *reinterpret_cast<u16x4*>(&ctx[(rowbase + i) * a.ldc + h * HD + d]) = u;
+      }
     }
+  }
 }
 
 template <typename T, int NW>
@@ -599,7 +664,7 @@ void attention(const AttnArgs& a, int mode, int head_dim, bool bf16, hipStream_t
   const double fl = pairs * 2.0 * head_dim * (mode == ATT_RELPOS ? 3 : 2);
   const double by = es * a.B * a.W * a.H * head_dim * 4.0;
   if (use_tp(a, mode, head_dim, bf16)) {
-    dim3 grid((a.W + 63) / 64, a.H, a.B);
+    dim3 grid((a.W + 127) / 128, a.H, a.B);
     if (mode == ATT_RELPOS)
       klaunch(PROF_ATTN, fl, by, attn_tp_kernel<64, ATT_RELPOS>, grid, dim3(256), s, a);
     else

@@ -8,15 +8,18 @@ typedef uint16_t bf16_t;  // bf16 storage (upper half of an fp32)
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
 #define SF_WAVE 64
 
 __device__ __forceinline__ float bf2f(bf16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
-// round to nearest even (inputs are finite)
-__device__ __forceinline__ bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+// round to nearest even (the hardware conversion, v_cvt_pk_bf16_f32)
+__device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+// eight floats to one bf16 MFMA operand (four packed conversions)
+__device__ __forceinline__ bf16x8_t pack_bf16x8(const float* v) {
+  const f32x8 f = {v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]};
+  return __builtin_convertvector(f, bf16x8_t);
 }
 
 template <typename T> __device__ __forceinline__ float to_f(T v);
