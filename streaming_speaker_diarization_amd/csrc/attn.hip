@@ -200,19 +200,28 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   for (int kt = w; kt < ntile; kt += NW) {
     const int j0 = kt * 64;
     load_v(j0);
-    // the loads are unconditional: zero what lies outside the head / window
+    // the loads are unconditional: zero what lies outside the head (head
+    // dims not a multiple of the k-step) or the position table (a band
+    // past either end: wave-uniform test)
+    if constexpr (HD % KI != 0) {
 #pragma unroll
-    for (int ks = 0; ks < NQF; ++ks) {
-      const unsigned dm = dim_mask(ks);
+      for (int ks = 0; ks < NQF; ++ks) {
+        const unsigned dm = dim_mask(ks);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) kf[nt][ks] = F::zero_if(kf[nt][ks], dm);
-      if constexpr (REL) {
-        const int dbase = iq0 - j0 - 63;
+        for (int nt = 0; nt < 4; ++nt) kf[nt][ks] = F::zero_if(kf[nt][ks], dm);
+      }
+    }
+    if constexpr (REL) {
+      const int dbase = iq0 - j0 - 63;
+      if (dbase < -a.p_center || dbase + 79 > a.p_center) {
 #pragma unroll
-        for (int ct = 0; ct < 5; ++ct) {
-          const int dl = dbase + 16 * ct + c16;
-          bfr[ct][ks] = F::zero_if(bfr[ct][ks], (dl >= -a.p_center && dl <= a.p_center) ? dm : 0u);
-        }
+        for (int ks = 0; ks < NQF; ++ks)
+#pragma unroll
+          for (int ct = 0; ct < 5; ++ct) {
+            const int dl = dbase + 16 * ct + c16;
+            bfr[ct][ks] =
+                F::zero_if(bfr[ct][ks], (dl >= -a.p_center && dl <= a.p_center) ? dim_mask(ks) : 0u);
+          }
       }
     }
     if constexpr (ROPE) {  // rotate the keys (positions = window index)
@@ -265,47 +274,69 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     }
     if (kt + NW < ntile) load_kb(j0 + 64 * NW);  // next tile of this wave, in flight now
 
-    // ---- online softmax (log2 domain)
+    // ---- online softmax (log2 domain: the running max is kept scaled by
+    // scale*log2(e), p = 2^(s*scale*log2(e) - m)); keys past n_valid exist
+    // only in the last tile
+    if (j0 + 64 > a.n_valid) {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          S[nt][r] = j0 + 16 * nt + c16 < a.n_valid ? S[nt][r] : -INFINITY;
+    }
     float mx[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) mx[r] = -INFINITY;
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const bool valid = j0 + 16 * nt + c16 < a.n_valid;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        S[nt][r] = valid ? S[nt][r] * sl2 : -INFINITY;
-        mx[r] = fmaxf(mx[r], S[nt][r]);
-      }
-    }
+    for (int r = 0; r < 4; ++r)
+      mx[r] = fmaxf(fmaxf(S[0][r], S[1][r]), fmaxf(S[2][r], S[3][r]));
     T* Pw = &Ps[w * 16 * LDP];
+    float alpha[4];
+    bool moved = false;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float mnew = fmaxf(mrow[r], row16_max(mx[r]));
-      const float alpha = exp2f(mrow[r] - mnew);
+      const float mnew = fmaxf(mrow[r], row16_max(mx[r]) * sl2);
+      alpha[r] = __builtin_amdgcn_exp2f(mrow[r] - mnew);
+      moved |= mnew != mrow[r];
       float rs = 0.f;
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const float p = exp2f(S[nt][r] - mnew);
+        const float p = __builtin_amdgcn_exp2f(fmaf(S[nt][r], sl2, -mnew));
         rs += p;
         Pw[(4 * g + r) * LDP + 16 * nt + c16] = from_f<T>(p);
       }
-      lrow[r] = lrow[r] * alpha + row16_sum(rs);
+      lrow[r] = lrow[r] * alpha[r] + row16_sum(rs);
       mrow[r] = mnew;
+    }
+    if (__ballot(moved)) {  // rescale only when some row's max moved
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) O[dt][r] *= alpha;
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) O[dt][r] *= alpha[r];
+    }
+    // V^T columns past the window (last tile) or the head are zero
+    if (j0 + 64 > a.W) {
+#pragma unroll
+      for (int ks = 0; ks < NKF; ++ks) {
+        unsigned km = 0;
+#pragma unroll
+        for (int e = 0; e < EPF; ++e) km |= (j0 + ks * KI + EPF * g + e < a.W ? 1u : 0u) << e;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) vf[dt][ks] = F::zero_if(vf[dt][ks], km);
+      }
+    }
+    if constexpr (HD % 16 != 0) {
+#pragma unroll
+      for (int ks = 0; ks < NKF; ++ks)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+          vf[dt][ks] = F::zero_if(vf[dt][ks], 16 * dt + c16 < HD ? 0xFFu : 0u);
     }
     wave_lds_sync();
-    // ---- O += P.V (V^T columns past the window or the head are zero)
+    // ---- O += P.V
 #pragma unroll
     for (int ks = 0; ks < NKF; ++ks) {
-      unsigned km = 0;
-#pragma unroll
-      for (int e = 0; e < EPF; ++e) km |= (j0 + ks * KI + EPF * g + e < a.W ? 1u : 0u) << e;
       const auto pa = M_::ld(&Pw[c16 * LDP + ks * KI], lane);
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-        O[dt] = M_::mma(pa, F::zero_if(vf[dt][ks], 16 * dt + c16 < HD ? km : 0u), O[dt]);
+      for (int dt = 0; dt < NDT; ++dt) O[dt] = M_::mma(pa, vf[dt][ks], O[dt]);
     }
   }
 
