@@ -84,8 +84,13 @@ void layernorm(const LnArgs& a, bool bf16, hipStream_t s);
 
 // Post-LN transformer layer tail (d = 192, FFN 768), bf16, up to 4096 rows:
 // x1 = LN1(x + ctx Wo^T + bo) written to x1 (fp32), and the FFN's output
-// projection as 4 fp32 partial sums over hidden chunks, part[c][M][192]
-// (bias b2 not included), for a LayerNorm with x_in = x1. Returns 4.
+// projection as fp32 partial sums over hidden chunks, part[c][M][192] (bias
+// b2 not included), for a LayerNorm with x_in = x1. wo, w1, w2 are in
+// fragment-major order (Arena::frag). Returns the number of chunks.
+#ifndef SF_TFT_NCH
+#define SF_TFT_NCH 4
+#define SF_TFT_NW 4
+#endif
 struct TfTailArgs {
   const void* ctx; const float* x; float* x1; int M;
   const void* wo; const float* bo; const float* g1; const float* be1;

@@ -49,6 +49,27 @@ struct Arena {
     }
     return dev + o;
   }
+  // bf16 copy of an N x K row-major matrix in MFMA fragment-major order: 1 KB
+  // block (t, s) = t * (K/32) + s holds rows 16t..16t+15, columns
+  // 32s..32s+31, lane l = 16 g + c's 8 values W[16t + c][32s + 8g + e] at
+  // element 8 l + e
+  const void* frag(const float* src, int N, int K) {
+    const size_t o = alloc((size_t)N * K * 2);
+    if (host && src) {
+      uint16_t* d = reinterpret_cast<uint16_t*>(host + o);
+      for (int t = 0; t < N / 16; ++t)
+        for (int sb = 0; sb < K / 32; ++sb)
+          for (int l = 0; l < 64; ++l)
+            for (int e = 0; e < 8; ++e) {
+              const float f = src[(size_t)(16 * t + l % 16) * K + 32 * sb + 8 * (l / 16) + e];
+              uint32_t u;
+              std::memcpy(&u, &f, 4);
+              u += 0x7FFFu + ((u >> 16) & 1u);
+              d[((size_t)t * (K / 32) + sb) * 512 + 8 * l + e] = (uint16_t)(u >> 16);
+            }
+    }
+    return dev + o;
+  }
   void* raw(size_t bytes) { return dev + alloc(bytes); }
 };
 
@@ -246,6 +267,11 @@ void build_sortformer(sf_model* m, Arena& A, const Src& s) {
     L.b2 = A.f32(s.get(p + "b2"), 192);
     L.ln2_g = A.f32(s.get(p + "ln2.g"), 192);
     L.ln2_b = A.f32(s.get(p + "ln2.b"), 192);
+    if (bf) {  // operand copies for the fused layer tail
+      L.wo_f = A.frag(s.get(p + "wo"), 192, 192);
+      L.w1_f = A.frag(s.get(p + "w1"), 768, 192);
+      L.w2_f = A.frag(s.get(p + "w2"), 192, 768);
+    }
   }
   {
     std::vector<float> w1t;
@@ -659,8 +685,8 @@ static void encode_sortformer(const sf_model* m, EncWs& w, int B, int W, int n_v
       // in the fp32 GLU buffer, which the transformer does not otherwise use)
       TfTailArgs t{};
       t.ctx = w.ctx; t.x = w.x; t.x1 = w.glu; t.M = B * W;
-      t.wo = L.wo; t.bo = L.bo; t.g1 = L.ln1_g; t.be1 = L.ln1_b;
-      t.w1 = L.w1; t.b1 = L.b1; t.w2 = L.w2; t.part = w.part;
+      t.wo = L.wo_f; t.bo = L.bo; t.g1 = L.ln1_g; t.be1 = L.ln1_b;
+      t.w1 = L.w1_f; t.b1 = L.b1; t.w2 = L.w2_f; t.part = w.part;
       const int nc = tf_tail(t, s);
       LnArgs n{};
       n.x = w.x; n.x_in = w.glu; n.M = B * W; n.D = 192;
