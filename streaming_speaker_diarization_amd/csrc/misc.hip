@@ -13,7 +13,7 @@ namespace sf {
 template <typename T, int D, int NS>
 __global__ __launch_bounds__(256) void ln_kernel(LnArgs a) {
   constexpr int PER = D / 64;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int row = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= a.M) return;
   float v[PER];
   float* xr = a.x + (size_t)row * D;
@@ -66,19 +66,22 @@ __global__ __launch_bounds__(256) void ln_kernel(LnArgs a) {
 }
 
 template <typename T, int D>
-static void ln_launch(const LnArgs& a, dim3 grid, hipStream_t s, double by) {
+static void ln_launch(const LnArgs& a, dim3 grid, dim3 block, hipStream_t s, double by) {
   switch (a.part ? a.nsplit : 0) {
-    case 0: klaunch(PROF_LN, 0.0, by, ln_kernel<T, D, 0>, grid, dim3(256), s, a); break;
-    case 1: klaunch(PROF_LN, 0.0, by, ln_kernel<T, D, 1>, grid, dim3(256), s, a); break;
-    case 2: klaunch(PROF_LN, 0.0, by, ln_kernel<T, D, 2>, grid, dim3(256), s, a); break;
-    case 3: klaunch(PROF_LN, 0.0, by, ln_kernel<T, D, 3>, grid, dim3(256), s, a); break;
-    case 4: klaunch(PROF_LN, 0.0, by, ln_kernel<T, D, 4>, grid, dim3(256), s, a); break;
-    case 6: klaunch(PROF_LN, 0.0, by, ln_kernel<T, D, 6>, grid, dim3(256), s, a); break;
-    case 8: klaunch(PROF_LN, 0.0, by, ln_kernel<T, D, 8>, grid, dim3(256), s, a); break;
+    case 0: klaunch(PROF_LN, 0.0, by, ln_kernel<T, D, 0>, grid, block, s, a); break;
+    case 1: klaunch(PROF_LN, 0.0, by, ln_kernel<T, D, 1>, grid, block, s, a); break;
+    case 2: klaunch(PROF_LN, 0.0, by, ln_kernel<T, D, 2>, grid, block, s, a); break;
+    case 3: klaunch(PROF_LN, 0.0, by, ln_kernel<T, D, 3>, grid, block, s, a); break;
+    case 4: klaunch(PROF_LN, 0.0, by, ln_kernel<T, D, 4>, grid, block, s, a); break;
+    case 6: klaunch(PROF_LN, 0.0, by, ln_kernel<T, D, 6>, grid, block, s, a); break;
+    case 8: klaunch(PROF_LN, 0.0, by, ln_kernel<T, D, 8>, grid, block, s, a); break;
     default: break;  // rejected by layernorm()
   }
 }
 
+#ifndef SF_LN_ROWS1
+#define SF_LN_ROWS1 1024
+#endif
 void layernorm(const LnArgs& a, bool bf16, hipStream_t s) {
   if (a.M <= 0) return;
   const int ns = a.part ? a.nsplit : 0;
@@ -88,13 +91,17 @@ void layernorm(const LnArgs& a, bool bf16, hipStream_t s) {
   }
   const double by = (double)a.M * a.D * (4.0 + 4.0 * ns + (a.x_mode ? 4.0 : 0.0) +
                                            (a.y_act ? (bf16 ? 2.0 : 4.0) : 0.0));
-  dim3 grid((a.M + 3) / 4);
+  // one row per wave; single-wave workgroups while that still leaves the
+  // grid within a few rounds of the 256 CUs (the loads of a row are then
+  // spread over more CUs), four-wave workgroups beyond
+  const int rpb = a.M <= SF_LN_ROWS1 ? 1 : 4;
+  const dim3 grid((a.M + rpb - 1) / rpb), block(64 * rpb);
   if (bf16) {
-    if (a.D == 512) ln_launch<bf16_t, 512>(a, grid, s, by);
-    else ln_launch<bf16_t, 192>(a, grid, s, by);
+    if (a.D == 512) ln_launch<bf16_t, 512>(a, grid, block, s, by);
+    else ln_launch<bf16_t, 192>(a, grid, block, s, by);
   } else {
-    if (a.D == 512) ln_launch<float, 512>(a, grid, s, by);
-    else ln_launch<float, 192>(a, grid, s, by);
+    if (a.D == 512) ln_launch<float, 512>(a, grid, block, s, by);
+    else ln_launch<float, 192>(a, grid, block, s, by);
   }
 }
 
