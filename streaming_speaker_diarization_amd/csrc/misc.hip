@@ -184,61 +184,59 @@ void dwconv_time(const float* glu, int B, int W, int n_valid, const float* w9, c
 #define MEL_TAB_LO 1424
 #define MEL_TAB_W 1680
 #define MELW 32
-// Frame t covers samples 160t-200 ... 160t+199 (the non-zero part of the
-// centred 512-point frame); samples outside [0, n_total) are zero. Each
-// workgroup computes 4 frames: |DFT|^2 for 257 bins, then the mel sums and
-// log(x + 2^-24).
+// Frame t covers samples 160t-200 ... 160t+199, the non-zero part of the
+// centred 512-point frame (window sample n at frame position n + 56); samples
+// outside [0, n_total) are zero. One workgroup per frame: the windowed frame
+// goes to LDS in bit-reversed order, a radix-2 decimation-in-time FFT (9
+// stages, one butterfly per thread each) gives the 257 bins, then |X|^2, the
+// sparse mel sums and log(x + 2^-24).
 __global__ __launch_bounds__(256) void logmel_kernel(const float* audio, long long a_bstride,
                                                      long long ring_mask, long long n_total,
                                                      long long t0, int nfr, const float* tab,
                                                      float* mel, long long m_bstride) {
-  __shared__ float xs[4][400];
-  __shared__ float tc[512], ts[512];
-  __shared__ float pw[4][257];
-  const int tid = threadIdx.x, b = blockIdx.y, f0 = blockIdx.x * 4;
+  __shared__ float xr[512], xi[512];
+  __shared__ float tc[256], ts[256];
+  __shared__ float pw[257];
+  const int tid = threadIdx.x, b = blockIdx.y, fr = blockIdx.x;
   const float* ab = audio + (size_t)b * a_bstride;
-  for (int i = tid; i < 512; i += 256) { tc[i] = tab[i]; ts[i] = tab[512 + i]; }
-  {
-    float v[7];
+  tc[tid] = tab[tid];
+  ts[tid] = tab[512 + tid];
 #pragma unroll
-    for (int q = 0; q < 7; ++q) {  // 7 x 256 >= 4 x 400 samples
-      const int i = min(tid + 256 * q, 4 * 400 - 1), f = i / 400, n = i % 400;
-      const long long smp = 160 * (t0 + f0 + f) - 200 + n;
-      const long long sc = smp < 0 ? 0 : (smp >= n_total ? n_total - 1 : smp);
-      v[q] = ab[sc & ring_mask];
-    }
-#pragma unroll
-    for (int q = 0; q < 7; ++q) {
-      const int i = tid + 256 * q;
-      if (i < 4 * 400) {
-        const int f = i / 400, n = i % 400;
-        const long long smp = 160 * (t0 + f0 + f) - 200 + n;
-        const bool live = f0 + f < nfr && smp >= 0 && smp < n_total;
-        xs[f][n] = live ? v[q] * tab[1024 + n] : 0.f;
-      }
-    }
+  for (int h = 0; h < 2; ++h) {
+    const int p = tid + 256 * h, n = p - 56;  // frame position, window sample
+    const long long smp = 160 * (t0 + fr) - 256 + p;
+    const long long sc = smp < 0 ? 0 : (smp >= n_total ? n_total - 1 : smp);
+    const float v = ab[sc & ring_mask];
+    const bool live = n >= 0 && n < 400 && smp >= 0 && smp < n_total;
+    const int q = (int)(__brev((unsigned)p) >> 23);
+    xr[q] = live ? v * tab[1024 + n] : 0.f;
+    xi[q] = 0.f;
   }
   __syncthreads();
-  for (int k = tid; k < 257; k += 256) {
-    float re[4] = {0.f, 0.f, 0.f, 0.f}, im[4] = {0.f, 0.f, 0.f, 0.f};
-    int idx = (k * 56) & 511;  // window sample n sits at frame position n+56
-    for (int n = 0; n < 400; ++n) {
-      const float c = tc[idx], s_ = ts[idx];
 #pragma unroll
-      for (int f = 0; f < 4; ++f) { re[f] += xs[f][n] * c; im[f] -= xs[f][n] * s_; }
-      idx = (idx + k) & 511;
-    }
-#pragma unroll
-    for (int f = 0; f < 4; ++f) pw[f][k] = re[f] * re[f] + im[f] * im[f];
+  for (int st = 0; st < 9; ++st) {
+    const int half = 1 << st, pos = tid & (half - 1);
+    const int i0 = ((tid >> st) << (st + 1)) + pos, i1 = i0 + half;
+    const int k = pos << (8 - st);  // twiddle exp(-2 pi i pos / (2 half)) = exp(-2 pi i k / 512)
+    const float c = tc[k], sn = ts[k];
+    const float ar = xr[i0], ai = xi[i0], br = xr[i1], bi = xi[i1];
+    const float tr = br * c + bi * sn, ti = bi * c - br * sn;
+    __syncthreads();
+    xr[i0] = ar + tr;
+    xi[i0] = ai + ti;
+    xr[i1] = ar - tr;
+    xi[i1] = ai - ti;
+    __syncthreads();
   }
+  pw[tid] = xr[tid] * xr[tid] + xi[tid] * xi[tid];
+  if (tid == 0) pw[256] = xr[256] * xr[256] + xi[256] * xi[256];
   __syncthreads();
-  for (int o = tid; o < 4 * 128; o += 256) {
-    const int f = o >> 7, m = o & 127;
-    if (f0 + f >= nfr) continue;
+  if (tid < 128 && fr < nfr) {
+    const int m = tid;
     const int lo = (int)tab[MEL_TAB_LO + 2 * m], cnt = (int)tab[MEL_TAB_LO + 2 * m + 1];
     float acc = 0.f;
-    for (int i = 0; i < cnt; ++i) acc += tab[MEL_TAB_W + m * MELW + i] * pw[f][lo + i];
-    mel[(size_t)b * m_bstride + (size_t)(f0 + f) * 128 + m] = logf(acc + 5.9604644775390625e-8f);
+    for (int i = 0; i < cnt; ++i) acc += tab[MEL_TAB_W + m * MELW + i] * pw[lo + i];
+    mel[(size_t)b * m_bstride + (size_t)fr * 128 + m] = logf(acc + 5.9604644775390625e-8f);
   }
 }
 
@@ -246,7 +244,7 @@ void logmel(const float* audio, long long a_bstride, long long ring_mask, long l
             long long t0, int nfr, int B, const float* tab, float* mel, long long m_bstride,
             hipStream_t s) {
   if (nfr <= 0) return;
-  dim3 grid((nfr + 3) / 4, B);
+  dim3 grid(nfr, B);
   klaunch(PROF_FRONTEND, (double)B * nfr * (2.0 * 2 * 400 * 257 + 2.0 * 257 * 2),
           (double)B * nfr * (160 * 4 + 128 * 4), logmel_kernel, grid, dim3(256), s, audio,
           a_bstride, ring_mask, n_total, (long long)t0, nfr, tab, mel, m_bstride);
