@@ -64,7 +64,7 @@ def parse():
 # counter runs, stored beside the rocprofv3 summaries together with a hash of
 # the kernel sources it was measured on; reported only while they match.
 PMC_FILE = os.path.join(ROOT, "profiles", "gemm_low60s_pmc.txt")
-PMC_SOURCES = ["gemm.hip", "kernels.h", "common.h"]
+PMC_SOURCES = ["gemm.hip", "tftail.hip", "kernels.h", "common.h"]
 
 
 def kernel_source_hash():
