@@ -10,36 +10,57 @@ namespace sf {
 // One wave per row; statistics in fp32 (two passes over registers). The
 // residual partials are summed in slice order, so the result does not depend
 // on scheduling.
+// Columns per lane: VW consecutive columns (16-byte accesses) at
+// VW*lane + 64*VW*i when D is a multiple of 256, else single columns.
 template <typename T, int D, int NS>
 __global__ __launch_bounds__(256) void ln_kernel(LnArgs a) {
   constexpr int PER = D / 64;
+  constexpr int VW = D % 256 == 0 ? 4 : 1;
+  constexpr int NV = PER / VW;
   const int row = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= a.M) return;
+  auto col = [&](int i) { return VW * lane + 64 * VW * (i / VW) + i % VW; };
+  auto ld = [&](const float* p, float* dst) {  // this lane's PER columns of a row
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      if constexpr (VW == 4) {
+        const float4 f = *reinterpret_cast<const float4*>(p + 4 * lane + 256 * j);
+        dst[4 * j] = f.x; dst[4 * j + 1] = f.y; dst[4 * j + 2] = f.z; dst[4 * j + 3] = f.w;
+      } else {
+        dst[j] = p[lane + 64 * j];
+      }
+    }
+  };
+  auto st = [&](float* p, const float* src) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      if constexpr (VW == 4)
+        *reinterpret_cast<float4*>(p + 4 * lane + 256 * j) =
+            make_float4(src[4 * j], src[4 * j + 1], src[4 * j + 2], src[4 * j + 3]);
+      else
+        p[lane + 64 * j] = src[j];
+    }
+  };
   float v[PER];
   float* xr = a.x + (size_t)row * D;
   const float* xin = (a.x_in ? a.x_in : a.x) + (size_t)row * D;
   // every load of the row (residual + NS partial slices) is issued before use
   float pp[NS > 0 ? NS : 1][PER];
+  ld(xin, v);
 #pragma unroll
-  for (int i = 0; i < PER; ++i) v[i] = xin[lane + 64 * i];
-#pragma unroll
-  for (int sp = 0; sp < NS; ++sp)
-#pragma unroll
-    for (int i = 0; i < PER; ++i) pp[sp][i] = a.part[((size_t)sp * a.M + row) * D + lane + 64 * i];
+  for (int sp = 0; sp < NS; ++sp) ld(a.part + ((size_t)sp * a.M + row) * D, pp[sp]);
   if constexpr (NS > 0) {
+    float pb[PER];
+    ld(a.pbias, pb);
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int c = lane + 64 * i;
       float t = 0.f;
 #pragma unroll
       for (int sp = 0; sp < NS; ++sp) t += pp[sp][i];
-      v[i] += a.alpha * (t + a.pbias[c]);
+      v[i] += a.alpha * (t + pb[i]);
     }
   }
-  if (a.x_mode == 1) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) xr[lane + 64 * i] = v[i];
-  }
+  if (a.x_mode == 1) st(xr, v);
   auto norm = [&](const float* gg, const float* bb) {
     float sm = 0.f;
 #pragma unroll
@@ -49,19 +70,31 @@ __global__ __launch_bounds__(256) void ln_kernel(LnArgs a) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) { v[i] -= mean; q += v[i] * v[i]; }
     const float rstd = 1.0f / sqrtf(wave_sum(q) * (1.0f / D) + 1e-5f);
+    float gv[PER], bv[PER];
+    ld(gg, gv);
+    ld(bb, bv);
 #pragma unroll
-    for (int i = 0; i < PER; ++i) v[i] = v[i] * rstd * gg[lane + 64 * i] + bb[lane + 64 * i];
+    for (int i = 0; i < PER; ++i) v[i] = v[i] * rstd * gv[i] + bv[i];
   };
   norm(a.g1, a.b1);
-  if (a.x_mode == 2) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) xr[lane + 64 * i] = v[i];
-  }
+  if (a.x_mode == 2) st(xr, v);
   if (a.g2) norm(a.g2, a.b2);
   if (a.y_act) {
     T* y = static_cast<T*>(a.y_act) + (size_t)row * D;
+    if constexpr (VW == 4 && sizeof(T) == 2) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) y[lane + 64 * i] = from_f<T>(v[i]);
+      for (int j = 0; j < NV; ++j) {
+        u16x4 u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[e] = f2bf(v[4 * j + e]);
+        *reinterpret_cast<u16x4*>(y + 4 * lane + 256 * j) = u;
+      }
+    } else if constexpr (VW == 4) {
+      st(reinterpret_cast<float*>(y), v);
+    } else {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) y[col(i)] = from_f<T>(v[i]);
+    }
   }
 }
 
