@@ -47,7 +47,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="low60s", choices=sorted(WORKLOADS))
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baselines")
+    ap.add_argument("--no-cpu-1thread", action="store_true",
+                    help="skip the single-thread CPU-oracle baseline")
     ap.add_argument("--no-profile", action="store_true", help="skip the profiled pass")
     ap.add_argument("--no-graphs", action="store_true",
                     help="launch the stream window forward kernel by kernel (no HIP graphs)")
@@ -169,6 +171,29 @@ class Runner:
                              self.audio[:, p:p + k].contiguous(), k, last) for p, k, last in plan]
         return self._chunks
 
+    def step_latency(self):
+        """Device time of each stream step of one pass (events on the launch
+        stream between steps): p50 / p95 / max in ms, or None offline."""
+        import numpy as np
+        import torch
+        if self.wl["mode"] != "stream":
+            return None
+        sf = self.sf
+        steps = self.chunks()
+        st = self.stream
+        st.reset()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(steps) + 1)]
+        e0 = 0
+        ev[0].record()
+        for i, (piece, k, last) in enumerate(steps):
+            buf = self.out[:, e0:] if self.B == 1 else st.out
+            e0 += sf.sortformer_stream_step(st.handle, piece, k, last, buf, st.ws)
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        t = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(len(steps))])
+        return {"p50": round(float(np.percentile(t, 50)), 4), "p95": round(float(np.percentile(t, 95)), 4),
+                "max": round(float(t.max()), 4), "steps": len(steps)}
+
     def one_pass(self):
         sf = self.sf
         if self.wl["mode"] == "offline":
@@ -188,8 +213,13 @@ class Runner:
             e0 += n
 
 
-def cpu_baseline(name, wl, audio_np):
-    """The oracle as it stands on a bounded sample of the same workload."""
+def cpu_baseline(name, wl, audio_np, one_thread=False):
+    """The oracle as it stands on a bounded sample of the same workload (BLAS
+    on every host core, or on one)."""
+    if one_thread:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            return cpu_baseline(name, wl, audio_np)
     import numpy as np
     try:
         from threadpoolctl import threadpool_info
@@ -268,6 +298,7 @@ def main():
     audio_s = audio_np.shape[0] * audio_np.shape[1] / 16000.0
     value = audio_s / (ms_per_step / 1e3)
 
+    lat = r.step_latency()
     prof = {}
     if not args.no_profile:
         sf = r.sf
@@ -320,7 +351,10 @@ def main():
                                "gbs": round(v["bytes"] / max(v["ms"], 1e-9) / 1e6, 1)}
                            for k, v in prof.items()},
         "roofline": roof,
+        "step_latency_ms": lat,
         "cpu_baseline": None if args.no_cpu else cpu_baseline(args.workload, wl, audio_np),
+        "cpu_baseline_1thread": (None if args.no_cpu or args.no_cpu_1thread else
+                                 cpu_baseline(args.workload, wl, audio_np, one_thread=True)),
     }
     print(json.dumps(line), flush=True)
 
