@@ -401,7 +401,19 @@ void attn_tp_kernel(AttnArgs a) {
   __shared__ float Gs[REL ? 4 * 80 * GP : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c16 = lane & 15;
-  const int iq0 = blockIdx.x * QB, h = blockIdx.y, b = blockIdx.z;
+  // XCD-aware order (bijection over the grid): physical workgroup i runs on
+  // XCD i % 8, and XCD x takes a contiguous range of the (stream, head, query
+  // block) order, so a stream's K, V^T and Q rows are fetched into one L2
+  int iq0, h, b;
+  {
+    const int gx = gridDim.x, gy = gridDim.y, total = gx * gy * gridDim.z;
+    const int pid = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+    const int q8 = total / 8, r8 = total % 8, xcd = pid % 8;
+    const int t = xcd * q8 + min(xcd, r8) + pid / 8;
+    iq0 = (t % gx) * QB;
+    h = (t / gx) % gy;
+    b = t / (gx * gy);
+  }
   const int iw = iq0 + 32 * w;  // this wave's first query row
   const bf16_t* qkv = static_cast<const bf16_t*>(a.qkv);
   const size_t rowbase = (size_t)b * a.W;
