@@ -149,7 +149,19 @@ template <typename T>
 __global__ __launch_bounds__(128) void dwconv_time_kernel(const float* glu, int W, int n_valid,
                                                           const float* w9, const float* sc,
                                                           const float* sh, T* out) {
-  const int t0 = blockIdx.x * DW_ROWS, b = blockIdx.y, c = threadIdx.x * 4;
+  // XCD-aware order (bijection over the grid): physical workgroup i runs on
+  // XCD i % 8, and XCD x takes a contiguous range of (stream, row block), so
+  // the halo rows that neighbouring blocks share come from one L2
+  int t0, b;
+  {
+    const int gx = gridDim.x, total = gx * gridDim.y;
+    const int pid = blockIdx.x + gx * blockIdx.y;
+    const int q8 = total / 8, r8 = total % 8, xcd = pid % 8;
+    const int t = xcd * q8 + min(xcd, r8) + pid / 8;
+    t0 = (t % gx) * DW_ROWS;
+    b = t / gx;
+  }
+  const int c = threadIdx.x * 4;
   const float* gb = glu + (size_t)b * W * 512 + c;
   float4 x[DW_ROWS + 8];
 #pragma unroll
