@@ -299,83 +299,139 @@ void logmel(const float* audio, long long a_bstride, long long ring_mask, long l
 // Layouts are channels-last: (rows, freq, 256). Row indices are absolute
 // within the utterance; a buffer holds rows [base, base+n). Input rows
 // outside [0, len_in) are the convolution's zero padding.
+// conv0: one workgroup = FB output frequencies of one output row of one
+// stream, thread = output channel; the 3 x (2 FB + 1) input patch they share
+// is staged in LDS once. Large batches take FB = 16 (fewer, longer
+// workgroups); a single stream keeps one frequency per workgroup so that its
+// few rows still spread over the chip. Every output is computed the same way
+// either way.
+template <int FB>
 __global__ __launch_bounds__(256) void conv0_kernel(const float* mel, long long mel_bstride,
                                                     int mel_base, int T, float* out,
                                                     long long out_bstride, int o_base,
                                                     const float* w, const float* bias) {
-  const int o = blockIdx.x / 64, f = blockIdx.x % 64, b = blockIdx.y, c = threadIdx.x;
+  constexpr int NJ = 2 * FB + 1;
+  __shared__ float xs[3][NJ];
+  const int o = blockIdx.x / (64 / FB), f0 = (blockIdx.x % (64 / FB)) * FB;
+  const int b = blockIdx.y, c = threadIdx.x;
   const float* mb = mel + (size_t)b * mel_bstride;
   const int r0 = 2 * (o_base + o) - 1;
   const int rlo = max(r0, max(0, mel_base)), rhi = min(r0 + 2, T - 1);
-  float x[9];
+  auto in_at = [&](int a, int j) {
+    const int r = min(max(r0 + a, rlo), rhi), col = min(max(2 * f0 - 1 + j, 0), 127);
+    return mb[(size_t)(r - mel_base) * 128 + col];
+  };
+  float x1[3][3];  // FB = 1: the patch straight into registers (uniform loads)
+  if constexpr (FB == 1) {
 #pragma unroll
-  for (int a = 0; a < 3; ++a)
+    for (int a = 0; a < 3; ++a)
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      const int r = min(max(r0 + a, rlo), rhi), col = min(max(2 * f - 1 + q, 0), 127);
-      x[a * 3 + q] = mb[(size_t)(r - mel_base) * 128 + col];
-    }
-  float acc = bias[c];
+      for (int j = 0; j < 3; ++j) x1[a][j] = in_at(a, j);
+  } else {
+    if (c < 3 * NJ) xs[c / NJ][c % NJ] = in_at(c / NJ, c % NJ);
+  }
+  float wc[9];
 #pragma unroll
-  for (int a = 0; a < 3; ++a)
+  for (int k = 0; k < 9; ++k) wc[k] = w[c * 9 + k];
+  const float bc = bias[c];
+  if constexpr (FB > 1) __syncthreads();
+  float* ob = out + (size_t)b * out_bstride + ((size_t)o * 64 + f0) * 256 + c;
+#pragma unroll 4
+  for (int i = 0; i < FB; ++i) {
+    const int f = f0 + i;
+    float acc = bc;
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      const int r = r0 + a, col = 2 * f - 1 + q;
-      const bool live = r >= 0 && r < T && col >= 0 && col < 128;
-      acc += live ? w[c * 9 + a * 3 + q] * x[a * 3 + q] : 0.f;
-    }
-  out[(size_t)b * out_bstride + ((size_t)o * 64 + f) * 256 + c] = fmaxf(acc, 0.f);
+    for (int a = 0; a < 3; ++a)
+#pragma unroll
+      for (int q = 0; q < 3; ++q) {
+        const int r = r0 + a, col = 2 * f - 1 + q;
+        const bool live = r >= 0 && r < T && col >= 0 && col < 128;
+        const float xv = FB == 1 ? x1[a][q] : xs[a][2 * i + q];
+        acc += live ? wc[a * 3 + q] * xv : 0.f;
+      }
+    ob[(size_t)i * 256] = fmaxf(acc, 0.f);
+  }
 }
 
 void conv0(const float* mel, long long mel_bstride, int mel_base, int T, float* out,
            long long out_bstride, int o_base, int n_out, int B, const float* w, const float* b,
            hipStream_t s) {
   if (n_out <= 0) return;
-  hipLaunchKernelGGL(conv0_kernel, dim3(n_out * 64, B), dim3(256), 0, s, mel, mel_bstride,
-                     mel_base, T, out, out_bstride, o_base, w, b);
+  if ((long long)n_out * (64 / 16) * B >= 1024)
+    hipLaunchKernelGGL(conv0_kernel<16>, dim3(n_out * (64 / 16), B), dim3(256), 0, s, mel,
+                       mel_bstride, mel_base, T, out, out_bstride, o_base, w, b);
+  else
+    hipLaunchKernelGGL(conv0_kernel<1>, dim3(n_out * 64, B), dim3(256), 0, s, mel, mel_bstride,
+                       mel_base, T, out, out_bstride, o_base, w, b);
 }
 
-template <typename T>
+// Depthwise 3x3 stride 2: one workgroup = DW_FB output frequencies of one
+// output row of one stream, thread = channel (its 3 x (2 DW_FB + 1) inputs and
+// 9 weights in registers); DW_FB = 4 for large batches, 1 otherwise.
+template <typename T, int DW_FB>
 __global__ __launch_bounds__(256) void dw2d_kernel(const float* in, long long in_bstride,
                                                    int in_base, int len_in, int f_in, T* out,
                                                    long long out_bstride, int o_base,
                                                    const float* w, const float* bias) {
-  const int f_out = (f_in + 1) / 2;
-  const int o = blockIdx.x / f_out, f = blockIdx.x % f_out, b = blockIdx.y, c = threadIdx.x;
+  constexpr int NJ = 2 * DW_FB + 1;
+  const int f_out = (f_in + 1) / 2, nfb = (f_out + DW_FB - 1) / DW_FB;
+  const int o = blockIdx.x / nfb, f0 = (blockIdx.x % nfb) * DW_FB, b = blockIdx.y, c = threadIdx.x;
   const float* ib = in + (size_t)b * in_bstride;
   const int r0 = 2 * (o_base + o) - 1;
   const int rlo = max(r0, max(0, in_base)), rhi = min(r0 + 2, len_in - 1);
-  float x[9];
+  float x[3][NJ];
 #pragma unroll
   for (int a = 0; a < 3; ++a)
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      const int r = min(max(r0 + a, rlo), rhi), col = min(max(2 * f - 1 + q, 0), f_in - 1);
-      x[a * 3 + q] = ib[((size_t)(r - in_base) * f_in + col) * 256 + c];
+    for (int j = 0; j < NJ; ++j) {
+      const int r = min(max(r0 + a, rlo), rhi), col = min(max(2 * f0 - 1 + j, 0), f_in - 1);
+      x[a][j] = ib[((size_t)(r - in_base) * f_in + col) * 256 + c];
     }
-  float acc = bias[c];
+  float wc[9];
 #pragma unroll
-  for (int a = 0; a < 3; ++a)
+  for (int k = 0; k < 9; ++k) wc[k] = w[c * 9 + k];
+  const float bc = bias[c];
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      const int r = r0 + a, col = 2 * f - 1 + q;
-      const bool live = r >= 0 && r < len_in && col >= 0 && col < f_in;
-      acc += live ? w[c * 9 + a * 3 + q] * x[a * 3 + q] : 0.f;
-    }
-  out[(size_t)b * out_bstride + ((size_t)o * f_out + f) * 256 + c] = from_f<T>(acc);
+  for (int i = 0; i < DW_FB; ++i) {
+    const int f = f0 + i;
+    if (f >= f_out) break;
+    float acc = bc;
+#pragma unroll
+    for (int a = 0; a < 3; ++a)
+#pragma unroll
+      for (int q = 0; q < 3; ++q) {
+        const int r = r0 + a, col = 2 * f - 1 + q;
+        const bool live = r >= 0 && r < len_in && col >= 0 && col < f_in;
+        acc += live ? wc[a * 3 + q] * x[a][2 * i + q] : 0.f;
+      }
+    out[(size_t)b * out_bstride + ((size_t)o * f_out + f) * 256 + c] = from_f<T>(acc);
+  }
 }
 
 void dw2d(const float* in, long long in_bstride, int in_base, int len_in, int f_in, void* out,
           long long out_bstride, int o_base, int n_out, int B, const float* w, const float* b,
           bool bf16, hipStream_t s) {
   if (n_out <= 0) return;
-  dim3 grid(n_out * ((f_in + 1) / 2), B);
-  if (bf16)
-    hipLaunchKernelGGL((dw2d_kernel<bf16_t>), grid, dim3(256), 0, s, in, in_bstride, in_base,
-                       len_in, f_in, static_cast<bf16_t*>(out), out_bstride, o_base, w, b);
-  else
-    hipLaunchKernelGGL((dw2d_kernel<float>), grid, dim3(256), 0, s, in, in_bstride, in_base, len_in,
-                       f_in, static_cast<float*>(out), out_bstride, o_base, w, b);
+  const int f_out = (f_in + 1) / 2;
+  const bool wide = (long long)n_out * ((f_out + 3) / 4) * B >= 1024;
+  dim3 grid(n_out * (wide ? (f_out + 3) / 4 : f_out), B);
+  if (bf16) {
+    bf16_t* o = static_cast<bf16_t*>(out);
+    if (wide)
+      hipLaunchKernelGGL((dw2d_kernel<bf16_t, 4>), grid, dim3(256), 0, s, in, in_bstride, in_base,
+                         len_in, f_in, o, out_bstride, o_base, w, b);
+    else
+      hipLaunchKernelGGL((dw2d_kernel<bf16_t, 1>), grid, dim3(256), 0, s, in, in_bstride, in_base,
+                         len_in, f_in, o, out_bstride, o_base, w, b);
+  } else {
+    float* o = static_cast<float*>(out);
+    if (wide)
+      hipLaunchKernelGGL((dw2d_kernel<float, 4>), grid, dim3(256), 0, s, in, in_bstride, in_base,
+                         len_in, f_in, o, out_bstride, o_base, w, b);
+    else
+      hipLaunchKernelGGL((dw2d_kernel<float, 1>), grid, dim3(256), 0, s, in, in_bstride, in_base,
+                         len_in, f_in, o, out_bstride, o_base, w, b);
+  }
 }
 
 // 8x frame stacking: out[b*n + j][r*128 + m] = mel[8(e0+j)+r][m], zero past T.
