@@ -618,9 +618,15 @@ __global__ __launch_bounds__(256) void splitk_epi_kernel(GemmArgs g, const float
   const int m = blockIdx.x;
   const int ncol = EPI == EPI_GLU ? g.N / 2 : g.N;
   for (int c = threadIdx.x; c < ncol; c += 256) {
-    auto red = [&](int n) {
+    auto red = [&](int n) {  // slices summed in order; the first 16 loaded at once
+      float pv[16];
+#pragma unroll
+      for (int s = 0; s < 16; ++s) pv[s] = s < ns ? part[((size_t)s * g.M + m) * g.N + n] : 0.f;
       float v = 0.f;
-      for (int s = 0; s < ns; ++s) v += part[((size_t)s * g.M + m) * g.N + n];
+#pragma unroll
+      for (int s = 0; s < 16; ++s)
+        if (s < ns) v += pv[s];
+      for (int s = 16; s < ns; ++s) v += part[((size_t)s * g.M + m) * g.N + n];
       return v + (g.bias ? g.bias[n] : 0.f);
     };
     if constexpr (EPI == EPI_GLU) {

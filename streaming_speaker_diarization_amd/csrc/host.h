@@ -64,7 +64,7 @@ struct sf_model {
   const void* proj_w;
   const float* proj_b;
   sfh::TfLayer tf[18];
-  const float *h_w1t, *h_b1, *h_w2, *h_b2;
+  const float *h_w1f, *h_b1, *h_w2, *h_b2;
   float* pe;
   float* init_part;  // split-K scratch used while deriving the position tables
   // Nemotron

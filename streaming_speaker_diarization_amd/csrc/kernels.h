@@ -115,7 +115,7 @@ void dw2d(const float* in, long long in_bstride, int in_base, int len_in, int f_
 void stack8(const float* mel, long long mel_bstride, int mel_base, int T, int e0, int n, int B,
             void* out, bool bf16, hipStream_t s);
 
-void head_sortformer(const float* x, int M, const float* w1t, const float* b1, const float* w2,
+void head_sortformer(const float* x, int M, const float* w1f, const float* b1, const float* w2,
                      const float* b2, int S, float* probs, hipStream_t s);
 void head_nemotron(const float* x, int M, const float* hw, const float* hb, const float* uw,
                    const float* ub, float* p80, float* p10, hipStream_t s);

@@ -466,25 +466,36 @@ void stack8(const float* mel, long long mel_bstride, int mel_base, int T, int e0
 
 // --------------------------------------------------------------- heads
 // Sortformer head, fp32: sigmoid(W2 relu(W1 x + b1) + b2). One workgroup =
-// 16 rows: the 192x192 layer runs on fp32 MFMA (wave w computes output
-// columns 48w..48w+47, A rows from LDS, W1^T read straight from global), the
-// 192->S layer and the sigmoid on the vector units.
-__global__ __launch_bounds__(256) void head_sf_kernel(const float* x, int M, const float* w1t,
+// 16 rows, 8 waves: the 192x192 layer runs on fp32 MFMA, wave w computing
+// output columns 48(w%4).. +47 over half of K (w/4), the two halves summed in
+// LDS. W1 is stored fragment by fragment (fragment (ks, ct) = lanes' values
+// W1[16ct + l%16][4ks + l/16], 256 contiguous bytes), so each wave issues its
+// 72 weight loads at once, in flight with the x rows and W2 (staged in LDS).
+// The 192->S layer (S <= 8) gives each row 16 lanes (a DPP reduction), then
+// the sigmoid.
+__global__ __launch_bounds__(512) void head_sf_kernel(const float* x, int M, const float* w1f,
                                                       const float* b1, const float* w2,
                                                       const float* b2, int S, float* probs) {
-  __shared__ float xs[16][196], hs[16][196];
+  __shared__ float xs[16][196], hs[16][196], w2s[8][192];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r0 = blockIdx.x * 16;
-  const int c16 = lane & 15, kq = lane >> 4;
-  {
-    float4 v[3];
+  const int c16 = lane & 15, kq = lane >> 4, wc = w & 3, kh = w >> 2;
+  for (int i = tid; i < S * 192; i += 512) w2s[i / 192][i % 192] = w2[i];
+  float4 v[2];
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {  // 16 rows x 48 float4 = 3 per thread
-      const int i = tid + 256 * q, r = i / 48, c = (i % 48) * 4;
-      v[q] = *reinterpret_cast<const float4*>(x + (size_t)min(r0 + r, M - 1) * 192 + c);
-    }
+  for (int q = 0; q < 2; ++q) {  // 16 rows x 48 float4
+    const int i = min(tid + 512 * q, 767), r = i / 48, c = (i % 48) * 4;
+    v[q] = *reinterpret_cast<const float4*>(x + (size_t)min(r0 + r, M - 1) * 192 + c);
+  }
+  float wf[24][3];
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      const int i = tid + 256 * q, r = i / 48, c = (i % 48) * 4;
+  for (int ks = 0; ks < 24; ++ks)
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      wf[ks][j] = w1f[(size_t)((24 * kh + ks) * 12 + 3 * wc + j) * 64 + lane];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int i = tid + 512 * q, r = i / 48, c = (i % 48) * 4;
+    if (i < 768) {
       const bool live = r0 + r < M;
       xs[r][c] = live ? v[q].x : 0.f;
       xs[r][c + 1] = live ? v[q].y : 0.f;
@@ -496,36 +507,47 @@ __global__ __launch_bounds__(256) void head_sf_kernel(const float* x, int M, con
   f32x4 acc[3];
 #pragma unroll
   for (int j = 0; j < 3; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-  for (int k = 0; k < 192; k += 4) {
-    const float av = xs[c16][k + kq];
+#pragma unroll
+  for (int ks = 0; ks < 24; ++ks) {
+    const float av = xs[c16][4 * (24 * kh + ks) + kq];
 #pragma unroll
     for (int j = 0; j < 3; ++j)
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, w1t[(k + kq) * 192 + 48 * w + 16 * j + c16],
-                                                    acc[j], 0, 0, 0);
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, wf[ks][j], acc[j], 0, 0, 0);
   }
+  if (kh == 1) {  // upper K half: partial sums to LDS
 #pragma unroll
-  for (int j = 0; j < 3; ++j) {
-    const int n = 48 * w + 16 * j + c16;
-    const float bn = b1[n];
+    for (int j = 0; j < 3; ++j)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) hs[4 * kq + i][n] = fmaxf(acc[j][i] + bn, 0.f);
+      for (int i = 0; i < 4; ++i) hs[4 * kq + i][48 * wc + 16 * j + c16] = acc[j][i];
   }
   __syncthreads();
-  if (tid < 16 * S) {
-    const int r = tid / S, sp = tid % S;
-    if (r0 + r < M) {
-      float z = b2[sp];
-      for (int k = 0; k < 192; ++k) z += hs[r][k] * w2[sp * 192 + k];
-      probs[(size_t)(r0 + r) * S + sp] = 1.0f / (1.0f + expf(-z));
+  if (kh == 0) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const int n = 48 * wc + 16 * j + c16;
+      const float bn = b1[n];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hs[4 * kq + i][n] = fmaxf(acc[j][i] + hs[4 * kq + i][n] + bn, 0.f);
+    }
+  }
+  __syncthreads();
+  if (tid < 256) {
+    const int r = tid >> 4, sub = tid & 15;  // 16 lanes per row
+    for (int sp = 0; sp < S; ++sp) {
+      float z = 0.f;
+#pragma unroll
+      for (int k = sub; k < 192; k += 16) z += hs[r][k] * w2s[sp][k];
+      z = row16_sum(z);
+      if (sub == 0 && r0 + r < M)
+        probs[(size_t)(r0 + r) * S + sp] = 1.0f / (1.0f + expf(-(z + b2[sp])));
     }
   }
 }
 
-void head_sortformer(const float* x, int M, const float* w1t, const float* b1, const float* w2,
+void head_sortformer(const float* x, int M, const float* w1f, const float* b1, const float* w2,
                      const float* b2, int S, float* probs, hipStream_t s) {
-  if (M <= 0) return;
-  hipLaunchKernelGGL(head_sf_kernel, dim3((M + 15) / 16), dim3(256), 0, s, x, M, w1t, b1, w2, b2, S,
+  if (M <= 0 || S < 1 || S > 8) return;
+  hipLaunchKernelGGL(head_sf_kernel, dim3((M + 15) / 16), dim3(512), 0, s, x, M, w1f, b1, w2, b2, S,
                      probs);
 }
 

@@ -274,14 +274,18 @@ void build_sortformer(sf_model* m, Arena& A, const Src& s) {
     }
   }
   {
-    std::vector<float> w1t;
+    // fp32 MFMA fragment order: fragment (ks, ct) holds, for lane l,
+    // W1[16ct + l%16][4ks + l/16]
+    std::vector<float> w1f;
     if (have) {
-      w1t.resize(192 * 192);
+      w1f.resize(192 * 192);
       const float* w = s.get("head.w1");
-      for (int n = 0; n < 192; ++n)
-        for (int k = 0; k < 192; ++k) w1t[k * 192 + n] = w[n * 192 + k];
+      for (int ks = 0; ks < 48; ++ks)
+        for (int ct = 0; ct < 12; ++ct)
+          for (int l = 0; l < 64; ++l)
+            w1f[((size_t)ks * 12 + ct) * 64 + l] = w[(16 * ct + l % 16) * 192 + 4 * ks + l / 16];
     }
-    m->h_w1t = A.f32(have ? w1t.data() : nullptr, 192 * 192);
+    m->h_w1f = A.f32(have ? w1f.data() : nullptr, 192 * 192);
     m->h_b1 = A.f32(s.get("head.b1"), 192);
     m->h_w2 = A.f32(s.get("head.w2"), (size_t)m->cfg.n_spk * 192);
     m->h_b2 = A.f32(s.get("head.b2"), m->cfg.n_spk);
@@ -703,7 +707,7 @@ static void encode_sortformer(const sf_model* m, EncWs& w, int B, int W, int n_v
     tp.at(17 + l, SF_TAP_LAYER_OUT, w.x, false, 192);
     hin = w.h;
   }
-  head_sortformer(w.x, B * W, m->h_w1t, m->h_b1, m->h_w2, m->h_b2, m->cfg.n_spk, w.probs, s);
+  head_sortformer(w.x, B * W, m->h_w1f, m->h_b1, m->h_w2, m->h_b2, m->cfg.n_spk, w.probs, s);
 }
 
 static void encode_nemotron(const sf_model* m, EncWs& w, int B, int W, int n_valid,
