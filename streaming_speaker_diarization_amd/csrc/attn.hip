@@ -340,6 +340,24 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     }
   }
 
+  // Output projection fused (bf16 rel-pos layers): this wave's Wo fragments
+  // (output columns 128w.., the head's 64 input columns), in flight during
+  // the merge.
+  constexpr bool FWO = REL && sizeof(T) == 2 && HD == 64 && NW == 4;
+  const bool fwo = FWO && a.wo_f != nullptr;
+  bf16x8_t wof[FWO ? 8 : 1][2];
+  if constexpr (FWO) {
+    if (fwo) {
+      const bf16_t* wo = static_cast<const bf16_t*>(a.wo_f);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          wof[j][ks] = *reinterpret_cast<const bf16x8_t*>(
+              wo + ((size_t)(8 * w + j) * 16 + 2 * h + ks) * 512 + 8 * lane);
+    }
+  }
+
   // ---- merge the four waves' partial softmax states
   if (c16 == 0) {
 #pragma unroll
@@ -363,7 +381,29 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
       l += Ls[v][r] * f;
       acc += Os[v][r][d] * f;
     }
-    if (i < a.W) ctx[(rowbase + i) * a.ldc + h * HD + d] = from_f<T>(acc / l);
+    const T cv = from_f<T>(acc / l);
+    if (i < a.W) ctx[(rowbase + i) * a.ldc + h * HD + d] = cv;
+    if constexpr (FWO) Ps[r * 72 + d] = i < a.W ? cv : T(0);  // A operand of the projection
+  }
+  if constexpr (FWO) {
+    if (fwo) {  // part[h][row] = ctx_h(row) . Wo[:, 64h..64h+63]^T, 128 columns per wave
+      __syncthreads();
+      bf16x8_t af[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) af[ks] = M_::ld(&Ps[c16 * 72 + ks * 32], lane);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        f32x4 acc{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) acc = M_::mma(af[ks], wof[j][ks], acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = iq0 + 4 * g + r;
+          if (i < a.W)
+            a.part[((size_t)h * a.M + rowbase + i) * 512 + 128 * w + 16 * j + c16] = acc[r];
+        }
+      }
+    }
   }
 }
 
@@ -701,11 +741,20 @@ static bool use_tp(const AttnArgs& a, int mode, int hd, bool bf16) {
 
 void attention(const AttnArgs& a, int mode, int head_dim, bool bf16, hipStream_t s) {
   if (a.W <= 0 || a.B <= 0) return;
-  // scores (q.k), the relative-position term (q.p(i-j)) and P.V per head
+  if (a.wo_f && (!bf16 || mode != ATT_RELPOS || head_dim != 64 || a.H * head_dim != 512 ||
+                 !a.part || a.M != a.B * a.W || use_tp(a, mode, head_dim, bf16))) {
+    flag_launch_failure();  // the fused projection exists only in the latency form
+    return;
+  }
+  // scores (q.k), the relative-position term (q.p(i-j)) and P.V per head,
+  // plus the fused output projection (its weights and fp32 partials)
   const double pairs = (double)a.B * a.H * a.W * a.n_valid;
   const double es = bf16 ? 2 : 4;
-  const double fl = pairs * 2.0 * head_dim * (mode == ATT_RELPOS ? 3 : 2);
-  const double by = es * a.B * a.W * a.H * head_dim * 4.0;
+  const double rows = (double)a.B * a.W;
+  const double fl = pairs * 2.0 * head_dim * (mode == ATT_RELPOS ? 3 : 2) +
+                    (a.wo_f ? 2.0 * rows * 512 * 512 : 0.0);
+  const double by = es * a.B * a.W * a.H * head_dim * 4.0 +
+                    (a.wo_f ? 2.0 * 512 * 512 + 4.0 * a.H * rows * 512 : 0.0);
   if (use_tp(a, mode, head_dim, bf16)) {
     dim3 grid((a.W + 127) / 128, a.H, a.B);
     if (mode == ATT_RELPOS)

@@ -33,6 +33,7 @@ struct ConfLayer {
   const void *ff1_w1, *ff1_w2, *wqkv, *wo, *pw1, *pw2, *ff2_w1, *ff2_w2;
   const float *ff1_b1, *ff1_b2, *bqkv, *bo, *pw1_b, *pw2_b, *ff2_b1, *ff2_b2;
   const float *u, *v, *dw9, *dw_sc, *dw_sh;
+  const void* wo_f;  // bf16 fragment-major copy of wo (output projection fused into attention)
   float* wpos;  // fp32 positional projection (init only)
   void* P;      // (2*SF_MAX_WINDOW-1, 512) projected relative positions
 };

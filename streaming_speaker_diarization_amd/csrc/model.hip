@@ -171,6 +171,7 @@ void build_sortformer(sf_model* m, Arena& A, const Src& s) {
       L.bqkv = A.f32(have ? b.data() : nullptr, 1536);
     }
     L.wo = A.act(s.get(p + "att.wo"), 512 * 512, bf);
+    L.wo_f = bf ? A.frag(s.get(p + "att.wo"), 512, 512) : nullptr;
     L.bo = A.f32(s.get(p + "att.bo"), 512);
     L.u = A.f32(s.get(p + "att.u"), 512);
     L.v = A.f32(s.get(p + "att.v"), 512);
@@ -638,9 +639,13 @@ static void encode_sortformer(const sf_model* m, EncWs& w, int B, int W, int n_v
     a.B = B; a.H = 8; a.W = W; a.n_valid = n_valid;
     a.ub = L.u; a.vb = L.v; a.P = L.P; a.ldp = 512; a.p_center = SF_MAX_WINDOW - 1;
     a.ctx = w.ctx; a.ldc = 512; a.scale = 0.125f;
+    // windows in the latency form: the output projection's per-head partial
+    // sums come from the attention kernel itself
+    const bool fuse_wo = bf && B * W <= SLICE_MAX_ROWS;
+    if (fuse_wo) { a.wo_f = L.wo_f; a.part = w.part; a.M = B * W; }
     attention(a, ATT_RELPOS, 64, bf, s);
     tp.at(l, SF_TAP_ATTN_CTX, w.ctx, bf, 512);
-    ns = c.branch(w.ctx, 512, L.wo, 512, 512);
+    ns = fuse_wo ? 8 : c.branch(w.ctx, 512, L.wo, 512, 512);
     c.ln(512, ns, L.bo, 1.f, L.conv_g, L.conv_b, nullptr, nullptr, 1, w.h);
     // convolution module
     if (bf && B * W <= SLICE_MAX_ROWS) {
