@@ -340,10 +340,10 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     }
   }
 
-  // Output projection fused (bf16 rel-pos layers): this wave's Wo fragments
+  // Output projection fused (bf16 rel-pos and rotary layers): this wave's Wo fragments
   // (output columns 128w.., the head's 64 input columns), in flight during
   // the merge.
-  constexpr bool FWO = REL && sizeof(T) == 2 && HD == 64 && NW == 4;
+  constexpr bool FWO = (REL || ROPE) && sizeof(T) == 2 && HD == 64 && NW == 4;
   const bool fwo = FWO && a.wo_f != nullptr;
   bf16x8_t wof[FWO ? 8 : 1][2];
   if constexpr (FWO) {
@@ -741,7 +741,7 @@ static bool use_tp(const AttnArgs& a, int mode, int hd, bool bf16) {
 
 void attention(const AttnArgs& a, int mode, int head_dim, bool bf16, hipStream_t s) {
   if (a.W <= 0 || a.B <= 0) return;
-  if (a.wo_f && (!bf16 || mode != ATT_RELPOS || head_dim != 64 || a.H * head_dim != 512 ||
+  if (a.wo_f && (!bf16 || mode == ATT_PLAIN || head_dim != 64 || a.H * head_dim != 512 ||
                  !a.part || a.M != a.B * a.W || use_tp(a, mode, head_dim, bf16))) {
     flag_launch_failure();  // the fused projection exists only in the latency form
     return;

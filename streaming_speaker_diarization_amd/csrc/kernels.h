@@ -64,7 +64,7 @@ struct AttnArgs {
   const float* rope;                  // (max_window, hd/2) (cos, sin) pairs
   void* ctx; int ldc;                 // (B*W, ldc) output
   float scale;
-  // Optional (bf16 latency form, ATT_RELPOS, H*hd == 512): the output
+  // Optional (bf16 latency form, ATT_RELPOS / ATT_ROPE, H*hd == 512): the output
   // projection's partial sums per head, part[h][M][512] = ctx_h Wo[:, h]^T
   // (M = B*W rows, no bias), with wo_f the fragment-major Wo (Arena::frag).
   const void* wo_f; float* part; int M;

@@ -331,6 +331,7 @@ void build_nemotron(sf_model* m, Arena& A, const Src& s) {
     L.wqkv = A.act(have ? w.data() : nullptr, 1536 * 512, bf);
     L.bqkv = A.f32(have ? b.data() : nullptr, 1536);
     L.wo = A.act(s.get(p + "wo"), 512 * 512, bf);
+    L.wo_f = bf ? A.frag(s.get(p + "wo"), 512, 512) : nullptr;
     L.bo = A.f32(s.get(p + "bo"), 512);
     L.ln2_g = A.f32(s.get(p + "ln2.g"), 512);
     L.ln2_b = A.f32(s.get(p + "ln2.b"), 512);
@@ -728,9 +729,11 @@ static void encode_nemotron(const sf_model* m, EncWs& w, int B, int W, int n_val
     a.qkv = w.big; a.ldq = 1536; a.qoff = 0; a.koff = 512; a.vt = w.vt; a.vpitch = w.vpitch;
     a.B = B; a.H = 8; a.W = W; a.n_valid = n_valid; a.rope = m->rope;
     a.ctx = w.ctx; a.ldc = 512; a.scale = 0.125f;
+    const bool fuse_wo = bf && B * W <= SLICE_MAX_ROWS;  // as in the conformer layers
+    if (fuse_wo) { a.wo_f = L.wo_f; a.part = w.part; a.M = B * W; }
     attention(a, ATT_ROPE, 64, bf, s);
     tp.at(l, SF_TAP_ATTN_CTX, w.ctx, bf, 512);
-    int ns = c.branch(w.ctx, 512, L.wo, 512, 512);
+    int ns = fuse_wo ? 8 : c.branch(w.ctx, 512, L.wo, 512, 512);
     c.ln(512, ns, L.bo, 1.f, L.ln2_g, L.ln2_b, nullptr, nullptr, 1, w.h);   // pre-LN
     c.lin(w.h, 512, L.w1, L.b1, 2048, 512, w.big, 2048, EPI_GELU, bf);
     ns = c.branch(w.big, 2048, L.w2, 512, 2048);
