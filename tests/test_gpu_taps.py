@@ -113,6 +113,45 @@ def test_sortformer_bf16_layers_batched_throughput_form(rt):
         _sortformer_layers(w, got, b, layers, nv, f"bf16 B={B} W={W}")
 
 
+def test_sortformer_bf16_layers_batched_latency_form(rt):
+    """5 windows of 203 frames, 190 valid (1015 rows: the latency forms, with
+    the output projection fused into the attention epilogue): each stream
+    against the oracle, and one stream bit-identical to the same window
+    encoded alone (a row's arithmetic does not depend on the batch)."""
+    m = rt.Model("sortformer", "bf16", seed=0)
+    w = make_weights("sortformer", 0, bf16=True)
+    B, W, nv = 5, 203, 190
+    emb = np.random.default_rng(16).standard_normal((B, W, 512))
+    layers = [0, 16, 17, 34]
+    taps = [(L, p) for L in layers for p in (IN, CTX, OUT)]
+    got = _run_taps(m, emb, nv, taps, _sf_width)
+    for b in (0, 2, 4):
+        _sortformer_layers(w, got, b, layers, nv, f"bf16 B={B} W={W}")
+    alone = _run_taps(m, emb[3:4], nv, taps, _sf_width)
+    for k in taps:
+        assert np.array_equal(alone[k][0, :nv], got[k][3, :nv]), k
+
+
+def test_nemotron_bf16_layers_batched(rt):
+    """3 windows of 150 frames, 140 valid, through the rotary layers' fused
+    output projection."""
+    m = rt.Model("nemotron", "bf16", seed=1)
+    w = make_weights("nemotron", 1, bf16=True)
+    B, W, nv = 3, 150, 140
+    emb = np.random.default_rng(17).standard_normal((B, W, 512))
+    layers = [0, 30]
+    got = _run_taps(m, emb, nv, [(L, p) for L in layers for p in (IN, CTX, OUT)], lambda L: 512)
+    for b in range(B):
+        for L in layers:
+            x = got[(L, IN)][b]
+            ctx = ON.rope_context(w, L, x, nv)
+            out = ON.rope_layer(w, L, x, nv)
+            if L == 30:
+                out = ON.layer_norm(out, w["final_ln.g"], w["final_ln.b"])
+            _check(f"nemotron bf16 B={B} b={b} layer {L} ctx", got[(L, CTX)][b, :nv], ctx[:nv], "bf16")
+            _check(f"nemotron bf16 B={B} b={b} layer {L} out", got[(L, OUT)][b, :nv], out[:nv], "bf16")
+
+
 def test_bf16_tolerance_separates_a_relative_position_shift(rt, monkeypatch):
     """Planted mistake, in the oracle: p(i-j+1) instead of p(i-j). The GPU
     context must sit inside the bf16 bound of the true oracle and far outside
