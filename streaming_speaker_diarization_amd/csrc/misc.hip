@@ -44,9 +44,17 @@ __global__ __launch_bounds__(256) void ln_kernel(LnArgs a) {
   float v[PER];
   float* xr = a.x + (size_t)row * D;
   const float* xin = (a.x_in ? a.x_in : a.x) + (size_t)row * D;
-  // every load of the row (residual + NS partial slices) is issued before use
+  // every load of the row (residual + NS partial slices) and of the LayerNorm
+  // parameters is issued before use
   float pp[NS > 0 ? NS : 1][PER];
   ld(xin, v);
+  float gv1[PER], bv1[PER], gv2[PER], bv2[PER];
+  ld(a.g1, gv1);
+  ld(a.b1, bv1);
+  if (a.g2) {
+    ld(a.g2, gv2);
+    ld(a.b2, bv2);
+  }
 #pragma unroll
   for (int sp = 0; sp < NS; ++sp) ld(a.part + ((size_t)sp * a.M + row) * D, pp[sp]);
   if constexpr (NS > 0) {
@@ -61,7 +69,7 @@ __global__ __launch_bounds__(256) void ln_kernel(LnArgs a) {
     }
   }
   if (a.x_mode == 1) st(xr, v);
-  auto norm = [&](const float* gg, const float* bb) {
+  auto norm = [&](const float* gv, const float* bv) {
     float sm = 0.f;
 #pragma unroll
     for (int i = 0; i < PER; ++i) sm += v[i];
@@ -70,15 +78,12 @@ __global__ __launch_bounds__(256) void ln_kernel(LnArgs a) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) { v[i] -= mean; q += v[i] * v[i]; }
     const float rstd = 1.0f / sqrtf(wave_sum(q) * (1.0f / D) + 1e-5f);
-    float gv[PER], bv[PER];
-    ld(gg, gv);
-    ld(bb, bv);
 #pragma unroll
     for (int i = 0; i < PER; ++i) v[i] = v[i] * rstd * gv[i] + bv[i];
   };
-  norm(a.g1, a.b1);
+  norm(gv1, bv1);
   if (a.x_mode == 2) st(xr, v);
-  if (a.g2) norm(a.g2, a.b2);
+  if (a.g2) norm(gv2, bv2);
   if (a.y_act) {
     T* y = static_cast<T*>(a.y_act) + (size_t)row * D;
     if constexpr (VW == 4 && sizeof(T) == 2) {
