@@ -157,6 +157,8 @@ size_t sortformer_stream_workspace_bytes(const sf_model* model, const sf_stream_
 sf_status sortformer_stream_create(sf_model* model, const sf_stream_config* scfg, int32_t batch,
                                    void* d_state, size_t state_bytes, void* stream,
                                    sf_stream** out);
+/* Releases the host object (waits for the device first if window graphs were
+ * captured, since a replay may still be queued). */
 void sortformer_stream_destroy(sf_stream* st);
 /* Empty the cache/FIFO/audio history (a new recording); enqueued on stream. */
 sf_status sortformer_stream_reset(sf_stream* st, void* stream);
@@ -213,7 +215,10 @@ sf_status sortformer_stream_import(sf_stream* st, int32_t cache_len, int32_t fif
  * window shape into a HIP graph on an internal stream and replayed on the
  * caller's stream; the frontend, pre_encode and the cache update stay
  * direct launches. 0 launches every kernel directly. Results are identical
- * either way. Graphs are rebuilt if the workspace pointer changes. */
+ * either way. Graphs are kept for one workspace pointer at a time (at most two
+ * per window size): a step with another workspace, or turning the option
+ * off, first waits for the device once and releases the old graphs; steps
+ * with an unchanged workspace never synchronise the host. */
 #define SF_STREAM_OPT_GRAPHS 1
 sf_status sortformer_stream_set_option(sf_stream* st, int32_t option, int32_t value);
 

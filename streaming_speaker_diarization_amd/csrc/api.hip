@@ -114,7 +114,12 @@ void state_update(sf_stream* st, const float* probs, int W, int n_chunk, hipStre
   }
 }
 
+// Releases the cached graphs. A replay may still be queued on any stream the
+// caller used, so the device is drained first (only when graphs exist: the
+// workspace changed, graphs were switched off, or the state is destroyed).
 void drop_graphs(sf_stream* st) {
+  if (st->graphs.empty()) return;
+  (void)hipDeviceSynchronize();
   for (auto& kv : st->graphs) (void)hipGraphExecDestroy(static_cast<hipGraphExec_t>(kv.second));
   st->graphs.clear();
 }
@@ -131,6 +136,10 @@ void window_forward(sf_stream* st, EncWs& enc, hipStream_t s) {
 // capture or instantiation failed (then the direct launch path was used).
 bool window_forward_graph(sf_stream* st, EncWs& enc, const void* ws, hipStream_t s) {
   const int W = st->Lc + st->Lf + st->Lp;
+  if (ws != st->graph_ws) {  // graphs of one workspace at a time: at most 2 per window size
+    drop_graphs(st);
+    st->graph_ws = ws;
+  }
   const auto key = std::make_tuple(W, st->cur, ws);
   auto it = st->graphs.find(key);
   if (it == st->graphs.end()) {
@@ -391,6 +400,7 @@ sf_status sortformer_stream_create(sf_model* m, const sf_stream_config* c, int32
   st->ring_cap = ring_cap_for(c);
   st->use_graphs = true;
   st->cap_stream = nullptr;
+  st->graph_ws = nullptr;
   bind_state(st, static_cast<char*>(d_state));
   reset_host(st);
   reset_device(st, HS(stream));

@@ -102,4 +102,5 @@ struct sf_stream {
   bool use_graphs;
   void* cap_stream;                                            // hipStream_t
   std::map<std::tuple<int, int, const void*>, void*> graphs;   // hipGraphExec_t
+  const void* graph_ws;  // the workspace the cached graphs were captured with
 };

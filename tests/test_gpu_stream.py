@@ -299,6 +299,23 @@ def test_graph_replays_match_direct_launches(rt, sf, sfbf):
         torch.cuda.synchronize()
         _ = (torch.randn(1000, device="cuda") * 2).sum().item()   # eager work in between
         assert np.array_equal(got, ref), f"replay {rep}"
+    # a step with another workspace releases the cached graphs and captures
+    # new ones; the workspace holds nothing across steps: results unchanged
+    st.reset()
+    ws_a, ws_b = st.ws, torch.full_like(st.ws, 0x7F)
+    outs, pos, n, k = [], 0, audio.shape[1], 0
+    while True:
+        st.ws = ws_b if (k // 5) % 2 else ws_a
+        need = st.samples_needed()
+        if pos + need > n:
+            outs.append(st.step(audio[:, pos:n], is_last=True).clone())
+            break
+        outs.append(st.step(audio[:, pos:pos + need]).clone())
+        pos += need
+        k += 1
+    st.ws = ws_a
+    assert k > 10
+    assert np.array_equal(torch.cat(outs, dim=1).cpu().numpy(), ref), "workspace switches"
     b = sfbf.stream("ultra_low", batch=3)
     a3 = _cuda(np.stack([meeting_audio(8.0, 2, 90 + i) for i in range(3)]))
     sf.sortformer_stream_set_option(b.handle, sf.SF_STREAM_OPT_GRAPHS, 0)
