@@ -22,6 +22,9 @@ namespace sf {
 
 #define CMP_MAXM 1024
 #define CMP_MAXS 8
+// candidates (cache + popped frames) and cache slots never exceed the state's
+// capacity, which the ABI bounds by the largest window
+static_assert(CMP_MAXM >= SF_MAX_WINDOW, "compression arrays must hold a full window");
 
 __global__ __launch_bounds__(512) void compress_kernel(const float* E, const float* P,
                                                        const int* ph, int cap, int D, int S,
