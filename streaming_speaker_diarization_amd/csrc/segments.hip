@@ -16,13 +16,15 @@ namespace sf {
 struct SegState {
   double ps, pe;  // pending segment
   bool have;
-  long long n;    // segments written
+  long long n;    // segments found (written while below the capacity, which the
+                  // host sizes for the most a track can hold)
+  long long cap;
 };
 
 __device__ __forceinline__ void seg_emit(SegState& st, double min_on, sf_segment* out, int spk,
                                          int b, bool writer) {
   if (st.have && st.pe - st.ps >= min_on) {
-    if (writer) {
+    if (writer && st.n < st.cap) {
       sf_segment sg;
       sg.start_s = st.ps;
       sg.end_s = st.pe;
@@ -58,7 +60,7 @@ __global__ __launch_bounds__(64) void segments_kernel(const float* probs, int T,
   sf_segment* o = out + (size_t)track * cap;
   const double total = (double)T * dt;
   const unsigned long long le = lane == 63 ? ~0ull : ((1ull << (lane + 1)) - 1ull);
-  SegState st{0.0, 0.0, false, 0};
+  SegState st{0.0, 0.0, false, 0, cap};
   unsigned long long carry = 0;  // state of the frame before this chunk
   int run0 = 0;                  // start frame of the open run
   constexpr int U = 16;  // chunks whose loads are issued together
