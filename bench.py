@@ -1,11 +1,13 @@
 """Benchmark of the streaming diarization forward on one MI355X.
 
 One benchmark step = one pass of the whole hot path over one synthetic
-workload: for the default workload (Streaming Sortformer, 'low' preset,
-60 s of 4-speaker meeting-like audio, bf16) that is the live stream of 124
-steps, each running the log-mel frontend and pre_encode on the new audio,
-the encoder over [cache | FIFO | chunk | look-ahead], the head, the FIFO
-update and (when the cache overflows) the compression.
+workload. For the default workload (64 independent streams of 120 s of
+4-speaker meeting-like audio, Streaming Sortformer 'ultra low' preset
+3/1/188/144/188, bf16, the streams in lockstep) that is the live stream of
+500 steps, each running, for all 64 streams at once, the log-mel frontend
+and pre_encode on the new audio, the encoder over [cache | FIFO | chunk |
+look-ahead] (64 windows of up to 378 frames), the head, the FIFO update and
+(when the cache overflows) the compression.
 
 value = RTFx = audio seconds processed / wall seconds, with the audio already
 resident in device memory. The JSON line also carries the dominant kernel
@@ -46,10 +48,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="low60s", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="ultralow64x120s", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baselines")
-    ap.add_argument("--no-cpu-1thread", action="store_true",
-                    help="skip the single-thread CPU-oracle baseline")
+    ap.add_argument("--cpu-1thread", action="store_true",
+                    help="also time the CPU oracle with one BLAS thread")
     ap.add_argument("--no-profile", action="store_true", help="skip the profiled pass")
     ap.add_argument("--no-graphs", action="store_true",
                     help="launch the stream window forward kernel by kernel (no HIP graphs)")
@@ -59,13 +61,25 @@ def parse():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the "
                          "calibration kernel for the HBM byte counters) and exit")
+    ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_DIR"),
+                    help="write the GEMM-class HBM-traffic summary of the workload from "
+                         "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of --window-probe and "
+                         "of --copy-probe (COPY_DIR holds copy_fetch/ and copy_write/) and exit")
     return ap.parse_args()
+
+
+def progress(msg):
+    """Progress of the run on stderr (the JSON line stays alone on stdout)."""
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
 # HBM traffic of the dominant kernel class from the FETCH_SIZE / WRITE_SIZE
 # counter runs, stored beside the rocprofv3 summaries together with a hash of
 # the kernel sources it was measured on; reported only while they match.
-PMC_FILE = os.path.join(ROOT, "profiles", "gemm_low60s_pmc.txt")
+def pmc_file(workload):
+    return os.path.join(ROOT, "profiles", f"gemm_{workload}_pmc.txt")
+
+
 PMC_SOURCES = ["gemm.hip", "tftail.hip", "kernels.h", "common.h"]
 
 
@@ -81,7 +95,7 @@ def kernel_source_hash():
 def measured_traffic(workload, kernel):
     """HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE), or None."""
     try:
-        kv = dict(line.split(":", 1) for line in open(PMC_FILE) if ":" in line)
+        kv = dict(line.split(":", 1) for line in open(pmc_file(workload)) if ":" in line)
     except OSError:
         return None
     kv = {k.strip(): v.strip() for k, v in kv.items()}
@@ -139,37 +153,27 @@ class Runner:
         S = self.model.n_spk
         if wl["mode"] == "stream":
             self.stream = self.model.stream(wl["preset"], batch=B)
-            # slack of one step's maximum emission: a step may be handed the
-            # tail of this buffer directly (B == 1)
-            max_emit = sf.sortformer_stream_max_emit(self.stream.handle)
-            self.out = torch.empty(B, te + max_emit, S, dtype=torch.float32, device="cuda")
+            n_out = te if wl["arch"] == "sortformer" else 8 * te
+            self.out = torch.empty(B, n_out, S, dtype=torch.float32, device="cuda")
         else:
             self.ws = self.model.workspace(
                 sf.sortformer_offline_workspace_bytes(self.model.handle, B, N))
             n_out = te if wl["arch"] == "sortformer" else 8 * te
             self.out = torch.empty(B, n_out, S, dtype=torch.float32, device="cuda")
 
-    def chunks(self):
-        """The live schedule's audio pieces as contiguous (B, k) device tensors,
-        prepared once outside the timed region (a column slice of a batch is
-        strided). For B == 1 the slices are views."""
-        if getattr(self, "_chunks", None) is None:
-            sf, st = self.sf, self.stream
-            st.reset()
-            plan, pos, N = [], 0, self.N
-            while True:
-                need = sf.sortformer_stream_samples_needed(st.handle)
-                last = pos + need > N
-                k = N - pos if last else need
-                plan.append((pos, k, last))
-                sf.sortformer_stream_step(st.handle, self.audio[:, pos:pos + k].contiguous(), k,
-                                          last, st.out, st.ws)
-                pos += k
-                if last:
-                    break
-            self._chunks = [(self.audio[:, p:p + k] if self.B == 1 else
-                             self.audio[:, p:p + k].contiguous(), k, last) for p, k, last in plan]
-        return self._chunks
+    def steps(self):
+        """The live schedule's audio pieces (start, count, is_last): the first
+        step needs 1280 * (chunk + look-ahead) + 40 samples, later ones 1280 *
+        chunk; the clip's end goes into the final step."""
+        c = self.stream.scfg
+        plan, pos = [], 0
+        while True:
+            need = 1280 * (c.chunk_len + c.right_context) + 40 if not plan else 1280 * c.chunk_len
+            if pos + need > self.N:
+                plan.append((pos, self.N - pos, True))
+                return plan
+            plan.append((pos, need, False))
+            pos += need
 
     def step_latency(self):
         """Device time of each stream step of one pass (events on the launch
@@ -178,44 +182,39 @@ class Runner:
         import torch
         if self.wl["mode"] != "stream":
             return None
-        sf = self.sf
-        steps = self.chunks()
-        st = self.stream
+        sf, st = self.sf, self.stream
+        plan = self.steps()
+        pieces = [self.audio[:, p:p + k].contiguous() for p, k, _ in plan]
         st.reset()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(steps) + 1)]
-        e0 = 0
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(plan) + 1)]
         ev[0].record()
-        for i, (piece, k, last) in enumerate(steps):
-            buf = self.out[:, e0:] if self.B == 1 else st.out
-            e0 += sf.sortformer_stream_step(st.handle, piece, k, last, buf, st.ws)
+        for i, (piece, (_, k, last)) in enumerate(zip(pieces, plan)):
+            sf.sortformer_stream_step(st.handle, piece, k, last, st.out, st.ws)
             ev[i + 1].record()
         torch.cuda.synchronize()
-        t = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(len(steps))])
+        t = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(len(plan))])
         return {"p50": round(float(np.percentile(t, 50)), 4), "p95": round(float(np.percentile(t, 95)), 4),
-                "max": round(float(t.max()), 4), "steps": len(steps)}
+                "max": round(float(t.max()), 4), "steps": len(plan)}
 
     def one_pass(self):
+        """The whole clip of every stream fed at once: the library runs the
+        live schedule's steps back to back, writing each step's emitted
+        frames into the output in order."""
         sf = self.sf
         if self.wl["mode"] == "offline":
             sf.sortformer_forward_offline(self.model.handle, self.audio, self.out, self.ws)
             return
-        steps = self.chunks()
         st = self.stream
         st.reset()
-        e0 = 0
-        h = st.handle
-        for piece, k, last in steps:
-            buf = self.out[:, e0:] if self.B == 1 else st.out
-            n = sf.sortformer_stream_step(h, piece, k, last, buf, st.ws)
-            if self.B > 1 and n:
-                S = self.out.shape[2]
-                self.out[:, e0:e0 + n].copy_(st.out.view(-1)[:self.B * n * S].view(self.B, n, S))
-            e0 += n
+        n = sf.sortformer_stream_feed(st.handle, self.audio, True, self.out, st.ws)
+        assert n == self.out.shape[1]
 
 
 def cpu_baseline(name, wl, audio_np, one_thread=False):
     """The oracle as it stands on a bounded sample of the same workload (BLAS
-    on every host core, or on one)."""
+    on every host core, or on one): frontend + pre_encode of one stream's clip
+    and a few steady-state stream steps, extrapolated to every step of every
+    stream of one pass."""
     if one_thread:
         from threadpoolctl import threadpool_limits
         with threadpool_limits(limits=1):
@@ -233,6 +232,7 @@ def cpu_baseline(name, wl, audio_np, one_thread=False):
     w = make_weights("sortformer", 0, bf16=(wl["dtype"] == "bf16"))
     cfg = streaming.StreamConfig.preset(wl["preset"])
     audio = audio_np[0]
+    B = audio_np.shape[0]
     t0 = time.perf_counter()
     emb = run.pre_encode_all(w, frontend.log_mel(audio))
     t_pre = time.perf_counter() - t0
@@ -245,25 +245,90 @@ def cpu_baseline(name, wl, audio_np, one_thread=False):
     rng = np.random.default_rng(0)
     st = streaming.State(emb[c0 - Lf - Lc:c0 - Lf].copy(), rng.random((Lc, 4)), np.zeros(Lc, bool),
                          emb[c0 - Lf:c0].copy(), rng.random((Lf, 4)), np.zeros(512), 0)
-    n_steps = min(8, len(sched) - k0)
+    n_steps = min(8 if B == 1 else 4, len(sched) - k0)
     enc = run.sortformer_encoder(w)
     t0 = time.perf_counter()
     for c0_, n, rc, last in sched[k0:k0 + n_steps]:
         streaming.stream_step(st, emb[c0_:c0_ + n + rc], n, cfg, enc, 4)
     t_step = (time.perf_counter() - t0) / n_steps
-    audio_s = len(audio) / 16000.0
-    total = t_pre + len(sched) * t_step
+    audio_s = B * len(audio) / 16000.0
+    total = B * (t_pre + len(sched) * t_step)
+    per = "" if B == 1 else f" per stream, times {B} streams"
     return {"value": audio_s / total, "unit": "x realtime (audio s / wall s)", "cores": threads,
             "kind": "oracle",
-            "sample": (f"oracle frontend+pre_encode of the whole {audio_s:.0f} s clip ({t_pre:.2f} s) "
-                       f"plus {n_steps} steady-state stream steps (W~{Lc + Lf + cfg.chunk_len + cfg.right_context}, "
-                       f"{t_step:.2f} s/step) extrapolated to the {len(sched)} steps of one pass")}
+            "sample": (f"oracle frontend+pre_encode of one {len(audio) / 16000:.0f} s clip "
+                       f"({t_pre:.2f} s) plus {n_steps} steady-state stream steps (W~"
+                       f"{Lc + Lf + cfg.chunk_len + cfg.right_context}, {t_step:.2f} s/step), "
+                       f"extrapolated to the {len(sched)} steps of one pass{per}")}
+
+
+def pmc_summary(name, fetch_dir, write_dir, copy_dir):
+    """GEMM-class HBM traffic per launch from rocprofv3 --pmc counter CSVs of
+    the window probe, calibrated by the same counters on a plain copy of
+    known size. Writes the summary that measured_traffic() reads."""
+    import csv
+    import glob
+
+    def rows(d, counter):
+        out = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r.get("Counter_Name") == counter:
+                    out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+        return out
+
+    def per_kernel(d, counter):
+        acc = {}
+        for k, v in rows(d, counter):
+            n, t = acc.get(k, (0, 0.0))
+            acc[k] = (n + 1, t + v)
+        return acc
+
+    cf = per_kernel(os.path.join(copy_dir, "copy_fetch"), "FETCH_SIZE")
+    cw = per_kernel(os.path.join(copy_dir, "copy_write"), "WRITE_SIZE")
+    copy_kib = 1024 * 1024  # the 1 GiB copy probe
+    ck = [k for k in cf if "copy" in k.lower()]
+    f_scale = copy_kib / (cf[ck[0]][1] / cf[ck[0]][0])
+    w_scale = copy_kib / (cw[ck[0]][1] / cw[ck[0]][0])
+    fe, wr = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+
+    def is_gemm(k):
+        return k.startswith(("gemm_", "splitk_epi", "tf_tail"))
+
+    n = sum(v[0] for k, v in fe.items() if is_gemm(k))
+    rd = sum(v[1] for k, v in fe.items() if is_gemm(k)) * 1024 * f_scale / max(n, 1)
+    wt = sum(v[1] for k, v in wr.items() if is_gemm(k)) * 1024 * w_scale / max(n, 1)
+    wl = WORKLOADS[name]
+    lines = [f"# GEMM kernel class: HBM traffic from FETCH_SIZE / WRITE_SIZE counters", "",
+             f"Workload: {name} ({wl['desc']}); counters taken on the encoder window probe",
+             "(bench.py --window-probe), one steady-state window per stream encoded twice.", "",
+             f"Calibration (1 GiB device copy {ck[0]}): FETCH_SIZE scale {f_scale:.4f}, "
+             f"WRITE_SIZE scale {w_scale:.4f}", "",
+             "Per kernel (KiB per dispatch, raw counter values):",
+             f"  {'kernel':60s} {'n':>5s} {'FETCH':>10s} {'WRITE':>10s}"]
+    for k in sorted(fe, key=lambda k: -fe[k][1]):
+        wv = wr.get(k, (1, 0.0))
+        lines.append(f"  {k[:60]:60s} {fe[k][0]:5d} {fe[k][1] / fe[k][0]:10.1f} "
+                     f"{wv[1] / max(wv[0], 1):10.1f}")
+    lines += ["", f"GEMM-class launches: {n}",
+              f"calibrated HBM read bytes per launch: {rd:.0f}",
+              f"calibrated HBM write bytes per launch: {wt:.0f}", "",
+              f"workload: {name}", "kernel_class: gemm",
+              f"kernel_sources_sha256: {kernel_source_hash()}",
+              f"hbm_bytes_per_launch: {rd + wt:.0f}"]
+    return "\n".join(lines) + "\n"
 
 
 def main():
     args = parse()
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.pmc_summary:
+        text = pmc_summary(args.workload, *args.pmc_summary)
+        with open(pmc_file(args.workload), "w") as f:
+            f.write(text)
+        print(text)
         return
     if args.window_probe:
         window_probe(args.workload, WORKLOADS[args.workload], args.window_probe)
@@ -275,21 +340,25 @@ def main():
     import numpy as np
     import torch
     wl = WORKLOADS[args.workload]
+    progress(f"workload {args.workload}: generating audio")
     audio_np = load_audio(args.workload, wl)
     audio = torch.from_numpy(audio_np.astype(np.float32)).cuda().contiguous()
+    progress("model init")
     r = Runner(args.workload, wl, audio)
     if args.no_graphs and wl["mode"] == "stream":
         r.sf.sortformer_stream_set_option(r.stream.handle, r.sf.SF_STREAM_OPT_GRAPHS, 0)
-    if wl["mode"] == "stream":
-        r.chunks()  # the schedule's audio pieces, before any timing
-    for _ in range(args.warmup):
+    for i in range(args.warmup):
         r.one_pass()
+        torch.cuda.synchronize()
+        progress(f"warm-up pass {i + 1}/{args.warmup} done")
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record()
-    for _ in range(args.steps):
+    for i in range(args.steps):
         r.one_pass()
+        if i % 5 == 4:
+            progress(f"timed pass {i + 1}/{args.steps} enqueued")
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -297,15 +366,17 @@ def main():
     ms_per_step = 1e3 * wall / args.steps
     audio_s = audio_np.shape[0] * audio_np.shape[1] / 16000.0
     value = audio_s / (ms_per_step / 1e3)
+    progress(f"timed: {ms_per_step:.1f} ms per pass, {value:.1f} x real time")
 
     lat = r.step_latency()
     prof = {}
     if not args.no_profile:
         sf = r.sf
         for kind in ("gemm", "attn", "ln", "conv", "frontend", "cache"):
-            sf.sortformer_profile_begin(kind, 200000)
+            sf.sortformer_profile_begin(kind, 400000)
             r.one_pass()
             prof[kind] = sf.sortformer_profile_end()
+            progress(f"profiled pass ({kind}) done")
         torch.cuda.synchronize()
     roof = None
     total_flops = sum(p["flops"] for p in prof.values())
@@ -326,7 +397,12 @@ def main():
             ach = p["bytes"] / max(p["launches"], 1) / (avg_ms / 1e3) / 1e9
             roof = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 2),
                     "peak": PEAK["hbm_gbs"], "unit": "GB/s", "frac": round(ach / PEAK["hbm_gbs"], 5),
-                    "traffic": measured_traffic(args.workload, dom), "launches": p["launches"], "avg_launch_us": round(1e3 * avg_ms, 3)}
+                    "traffic": measured_traffic(args.workload, dom), "launches": p["launches"],
+                    "avg_launch_us": round(1e3 * avg_ms, 3)}
+    cpu = None
+    if not args.no_cpu:
+        progress("CPU oracle sample")
+        cpu = cpu_baseline(args.workload, wl, audio_np)
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -352,9 +428,9 @@ def main():
                            for k, v in prof.items()},
         "roofline": roof,
         "step_latency_ms": lat,
-        "cpu_baseline": None if args.no_cpu else cpu_baseline(args.workload, wl, audio_np),
-        "cpu_baseline_1thread": (None if args.no_cpu or args.no_cpu_1thread else
-                                 cpu_baseline(args.workload, wl, audio_np, one_thread=True)),
+        "cpu_baseline": cpu,
+        "cpu_baseline_1thread": (cpu_baseline(args.workload, wl, audio_np, one_thread=True)
+                                 if args.cpu_1thread and not args.no_cpu else None),
     }
     print(json.dumps(line), flush=True)
 

@@ -92,19 +92,54 @@ sf_status sortformer_stream_preset(const char* name, sf_stream_config* out);
 
 /* ------------------------------------------------------------------ model */
 
-/* Device bytes the weights (plus derived tables) need; 0 if cfg is invalid. */
+/* Device bytes the weights (plus derived tables) need; 0 if cfg is invalid.
+ * The tensors are those of the "Streaming Sortformer Diarizer" model card's
+ * Pipeline and Model Parameters (117M parameters, about 470 MB in fp32), or of
+ * the Nemotron-3-Diarization summary in the ExecuTorch issue (about 100M). */
 size_t sortformer_weight_bytes(const sf_model_config* cfg);
 
-/* Generate the seeded random-init weights on the host (SplitMix64 counters +
- * Box-Muller, one stream per tensor), upload them into d_weights (caller
- * memory of >= sortformer_weight_bytes bytes, 256-byte aligned), derive the
- * device tables (relative-position projections, folded BatchNorm, DFT/mel
- * tables) and return a host handle. Blocks until the uploads are done.
- * d_weights must stay allocated until sortformer_free. */
+/* The model with seeded random weights: the pages run a trained checkpoint
+ * ("Streaming Sortformer Diarizer" model card, Pipeline; Transformers docs,
+ * Overview), which does not exist here, so every weight is drawn instead.
+ * Generates them on the host (SplitMix64 counters + Box-Muller, one stream
+ * per tensor), uploads them into d_weights (caller memory of >=
+ * sortformer_weight_bytes bytes, 256-byte aligned), derives the device tables
+ * (relative-position projections, folded BatchNorm, DFT/mel tables) and
+ * returns a host handle in *out. Blocks until the uploads are done.
+ * d_weights must stay allocated until sortformer_free. Errors: SF_EINVAL
+ * (null pointer, invalid cfg, misaligned d_weights), SF_ENOMEM
+ * (weight_bytes too small), SF_EHIP. */
 sf_status sortformer_init(const sf_model_config* cfg, uint64_t seed, void* d_weights,
                           size_t weight_bytes, void* stream, sf_model** out);
+/* Releases the host handle (the caller frees d_weights afterwards). NULL is
+ * ignored. */
 void sortformer_free(sf_model* model);
+/* The configuration the model was created with. SF_EINVAL on null pointers. */
 sf_status sortformer_get_config(const sf_model* model, sf_model_config* out);
+
+/* Model metadata: the constants the "Streaming Sortformer Diarizer" model
+ * card exports beside its methods (Exported Methods, Metadata:
+ * sample_rate, window_stride, subsampling_factor, fc_d_model, tf_d_model,
+ * max_num_of_spks, spkcache_len) and the frontend and layer sizes of the
+ * same card's Pipeline and Model Parameters. For NEMOTRON the encoder is the
+ * 31-layer rotary Transformer of width 512 (no FastConformer: fc_d_model 0)
+ * and the output runs at 10 ms. */
+typedef struct sf_model_metadata {
+  double window_stride;         /* seconds between mel frames: 0.01              */
+  double output_frame_s;        /* seconds per output frame: 0.08 or 0.01         */
+  int32_t sample_rate;          /* 16000                                          */
+  int32_t subsampling_factor;   /* mel frames per encoder frame: 8                */
+  int32_t fc_d_model;           /* FastConformer width: 512 (SORTFORMER), 0       */
+  int32_t tf_d_model;           /* Transformer width: 192 (SORTFORMER), 512       */
+  int32_t max_num_of_spks;      /* 4 (SORTFORMER), 8 (NEMOTRON)                   */
+  int32_t spkcache_len;         /* speaker-cache frames of every preset: 188      */
+  int32_t n_mels, n_fft, win_length, hop_length; /* 128, 512, 400, 160          */
+  int32_t n_conformer_layers;   /* 17 (SORTFORMER), 0                             */
+  int32_t n_transformer_layers; /* 18 (SORTFORMER), 31 (NEMOTRON)                 */
+  int32_t n_heads;              /* 8                                              */
+  int32_t max_window;           /* SF_MAX_WINDOW                                  */
+} sf_model_metadata;
+sf_status sortformer_get_metadata(const sf_model* model, sf_model_metadata* out);
 
 /* Canonical tensor list (name, element count) and the fp32 value of every
  * element as generated (before any bf16 rounding); for checking the weight
@@ -144,23 +179,38 @@ sf_status sortformer_forward_offline(sf_model* model, const float* d_audio, int3
 
 /* -------------------------------------------------------------- streaming */
 
-/* Device bytes of the per-stream state (speaker cache, FIFO, look-ahead
- * embeddings and their probabilities, placeholder flags, silence sums, audio
- * ring) for `batch` lockstep streams; and of the step workspace. */
+/* Device bytes of the per-stream state for `batch` lockstep streams: the
+ * speaker cache, FIFO and look-ahead embeddings with their probabilities and
+ * placeholder flags (NeMo API docs, SortformerStreamingState: spkcache,
+ * spkcache_preds, fifo, fifo_preds and their lengths; "Streaming Sortformer
+ * Diarizer" model card, Streaming Architecture), the silence statistics of
+ * the placeholders, and the audio ring holding the samples the next mel
+ * frames need. And the step workspace. 0 if the configuration is invalid or
+ * its window (spkcache_len + fifo_len + chunk_len + right_context) exceeds
+ * SF_MAX_WINDOW. */
 size_t sortformer_state_bytes(const sf_model* model, const sf_stream_config* scfg,
                               int32_t batch);
 size_t sortformer_stream_workspace_bytes(const sf_model* model, const sf_stream_config* scfg,
                                          int32_t batch);
 
-/* Bind a state object to caller memory d_state and reset it. The B streams
- * advance in lockstep (identical lengths, per-stream contents). */
+/* Bind a state object to caller memory d_state (state_bytes bytes, 256-byte
+ * aligned, kept alive until destroy) and reset it: the state NeMo's
+ * forward_streaming_step threads through its calls (NeMo API docs,
+ * SortformerStreamingState) and the Transformers streaming loop passes back
+ * as speaker_cache (Transformers docs "Nemotron 3 Diarization", streaming
+ * usage), here device-resident. The B streams advance in lockstep (identical
+ * lengths, per-stream contents). Errors: SF_EINVAL (null pointer, invalid
+ * configuration, misalignment), SF_ESHAPE (window above SF_MAX_WINDOW or
+ * fewer than one cache slot per speaker), SF_ENOMEM (state too small), SF_EHIP. */
 sf_status sortformer_stream_create(sf_model* model, const sf_stream_config* scfg, int32_t batch,
                                    void* d_state, size_t state_bytes, void* stream,
                                    sf_stream** out);
 /* Releases the host object (waits for the device first if window graphs were
  * captured, since a replay may still be queued). */
 void sortformer_stream_destroy(sf_stream* st);
-/* Empty the cache/FIFO/audio history (a new recording); enqueued on stream. */
+/* Empty the cache/FIFO/audio history and every counter, for a new recording
+ * (the runner's "streaming feed, reset, and final-flush" duties, ExecuTorch
+ * issue, Proposed scope); enqueued on stream. */
 sf_status sortformer_stream_reset(sf_stream* st, void* stream);
 
 /* Samples per stream the next non-final step needs (like the Transformers
@@ -186,29 +236,81 @@ int32_t sortformer_stream_max_emit(const sf_stream* st);
 sf_status sortformer_stream_step(sf_stream* st, const float* d_audio_new, int64_t n_new,
                                  int32_t is_last, float* d_probs_out, int32_t* n_emitted_host,
                                  void* d_workspace, size_t workspace_bytes, void* stream);
+/* (step, continued) Errors, all returned before any work is enqueued:
+ * SF_ESTATE after the final step, on a rows-only stream (set_rows), with
+ * samples pending from sortformer_stream_feed, or when the counters would
+ * make the step's window exceed the state's capacity; SF_ESHAPE for a wrong
+ * n_new; SF_ENOMEM for a small workspace. */
 
-/* State introspection for checkpoint/resume and tests.
- * info (host, 8 values): cache_len, fifo_len, lookahead_len, capacity rows,
- *   steps_done, frames_emitted, samples_received, finished.
+/* Streaming feed of any sample count (the runner's "streaming feed, reset,
+ * and final-flush", ExecuTorch issue, Proposed scope; the Transformers
+ * streaming loop, which hands the processor audio as it arrives): the n_new
+ * samples per stream (d_audio_new (B, n_new)) are appended to the samples
+ * already pending, every step whose audio is then complete runs exactly as
+ * sortformer_stream_step would run it, and the rest stays pending in the
+ * state's audio ring for the next feed. With is_last != 0 the clip ends after
+ * these samples: the complete steps run, then the final step (no
+ * look-ahead, every remaining frame scored). The emitted frames of all steps
+ * run are written in order to d_probs_out (B, out_frames, S) at rows [0,
+ * *n_emitted) of each stream (batch stride out_frames * S floats); the same
+ * samples fed in any split give bit-identical outputs and state. Errors,
+ * returned before any work: SF_ENOMEM if out_frames (or the workspace) is
+ * too small, SF_ESTATE after the final step or on a rows-only stream. */
+sf_status sortformer_stream_feed(sf_stream* st, const float* d_audio_new, int64_t n_new,
+                                 int32_t is_last, float* d_probs_out, int64_t out_frames,
+                                 int64_t* n_emitted_host, void* d_workspace,
+                                 size_t workspace_bytes, void* stream);
+/* Frames per stream a feed of n_new samples would emit now (host arithmetic;
+ * -1 if the feed would be refused). */
+int64_t sortformer_stream_feed_frames(const sf_stream* st, int64_t n_new, int32_t is_last);
+
+/* State introspection for tests.
+ * info (host, 9 values): cache_len, fifo_len, lookahead_len, capacity rows,
+ *   steps_done, frames_emitted, samples_received, finished, samples pending
+ *   (fed but not yet consumed by a step).
  * ptrs (host, 6 values): device pointers of emb (B,cap,D) fp32, probs
  *   (B,cap,S) fp32, placeholder flags (B,cap) int32, silence sum (B,D) fp64,
  *   silence count (B) int32, and the model dimension D as an integer.
  * Rows [0,cache_len) are the cache, then the FIFO, then look-ahead rows. */
 sf_status sortformer_stream_get_info(const sf_stream* st, int64_t* info, void** ptrs);
-/* Checkpoint/resume of the cache content: copy the rows [0, cache_len +
- * fifo_len + lookahead_len) of the state to host memory (export) or from
- * host memory (import, which also sets the three lengths). Host layouts:
- * emb (B, rows, D) fp32, probs (B, rows, S) fp32, flags (B, rows) int32
- * (1 = silence placeholder), sil_sum (B, D) fp64, sil_cnt (B) int32.
- * Both block until the copies are done. Import checks the lengths against
- * the configuration (cache <= spkcache_len, fifo <= fifo_len, look-ahead <=
- * chunk_len + right_context). */
-sf_status sortformer_stream_export(const sf_stream* st, float* emb, float* probs, int32_t* flags,
-                                   double* sil_sum, int32_t* sil_cnt, void* stream);
-sf_status sortformer_stream_import(sf_stream* st, int32_t cache_len, int32_t fifo_len,
-                                   int32_t lookahead_len, const float* emb, const float* probs,
-                                   const int32_t* flags, const double* sil_sum,
-                                   const int32_t* sil_cnt, void* stream);
+/* Checkpoint / resume of the whole streaming state (NeMo API docs,
+ * SortformerStreamingState, which forward_streaming_step returns and takes
+ * back; the Transformers speaker_cache): cache, FIFO and look-ahead rows with
+ * their probabilities and placeholder flags, the silence statistics, the
+ * audio ring with any pending samples, and every counter (steps, frames
+ * emitted, samples received, frames pre-encoded, finished). The blob is
+ * host memory of at least sortformer_stream_checkpoint_bytes bytes, written
+ * by export in a versioned layout private to this library. Import restores
+ * it into any stream object of the same model architecture, speaker count,
+ * batch and stream configuration (a fresh one, or the same one rewound): the
+ * steps that follow are bit-identical to those of the exported stream.
+ * Import checks the header (magic, version, configuration) and the counters'
+ * consistency and returns SF_EINVAL with the stream untouched if either
+ * fails. Both block until their copies are done. Export of a stream whose
+ * rows were set by sortformer_stream_set_rows returns SF_ESTATE. */
+size_t sortformer_stream_checkpoint_bytes(const sf_stream* st);
+sf_status sortformer_stream_export(const sf_stream* st, void* host_blob, size_t bytes,
+                                   void* stream);
+sf_status sortformer_stream_import(sf_stream* st, const void* host_blob, size_t bytes,
+                                   void* stream);
+
+/* Test hooks — the rows alone: copy rows [0, cache_len + fifo_len +
+ * lookahead_len) of the state to host memory (get) or from host memory (set,
+ * which also sets the three lengths). Host layouts: emb (B, rows, D) fp32,
+ * probs (B, rows, S) fp32, flags (B, rows) int32 (1 = silence placeholder),
+ * sil_sum (B, D) fp64, sil_cnt (B) int32 (either may be NULL: not copied).
+ * Both block until the copies are done. set checks the lengths against the
+ * configuration (cache <= spkcache_len, fifo <= fifo_len, look-ahead <=
+ * chunk_len + right_context) and leaves the step counters alone, so the
+ * stream is marked rows-only: sortformer_stream_step, _feed and _export
+ * return SF_ESTATE (before any work) until sortformer_stream_reset or
+ * sortformer_stream_import; sortformer_stream_update is allowed. */
+sf_status sortformer_stream_get_rows(const sf_stream* st, float* emb, float* probs, int32_t* flags,
+                                     double* sil_sum, int32_t* sil_cnt, void* stream);
+sf_status sortformer_stream_set_rows(sf_stream* st, int32_t cache_len, int32_t fifo_len,
+                                     int32_t lookahead_len, const float* emb, const float* probs,
+                                     const int32_t* flags, const double* sil_sum,
+                                     const int32_t* sil_cnt, void* stream);
 
 /* Stream options. SF_STREAM_OPT_GRAPHS (default 1): each step's window
  * forward (window copy + encoder + head) is captured once per distinct
@@ -222,8 +324,9 @@ sf_status sortformer_stream_import(sf_stream* st, int32_t cache_len, int32_t fif
 #define SF_STREAM_OPT_GRAPHS 1
 sf_status sortformer_stream_set_option(sf_stream* st, int32_t option, int32_t value);
 
-/* Test hook — the cache update alone (FIFO prediction refresh, chunk append,
- * pop with silence statistics, compression), given window probabilities
+/* Test hook — the cache update alone ("Streaming Sortformer Diarizer" model
+ * card, Streaming Architecture: FIFO prediction refresh, chunk append, pop
+ * with silence statistics, compression), given window probabilities
  * d_window_probs (B, W, S) with W = cache_len + fifo_len + lookahead_len of
  * the current state; the first n_chunk look-ahead rows are the chunk. */
 sf_status sortformer_stream_update(sf_stream* st, const float* d_window_probs, int32_t n_chunk,

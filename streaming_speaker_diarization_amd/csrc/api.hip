@@ -78,9 +78,32 @@ void bind_state(sf_stream* st, char* base) {
 void reset_host(sf_stream* st) {
   st->cur = 0;
   st->Lc = st->Lf = st->Lp = 0;
-  st->steps = st->emitted = st->recv = 0;
+  st->steps = st->emitted = st->recv = st->pending = 0;
   st->enc_done = 0;
   st->finished = false;
+  st->rows_only = false;
+}
+
+// Lengths after the cache update of a step that scored n_chunk look-ahead
+// rows: FIFO append, the pop rule n = min(len, max(update_period, len -
+// fifo_len)) ("Streaming Sortformer Diarizer" model card, Streaming
+// Architecture and Configurations), and compression back to spkcache_len.
+struct Lens {
+  int Lc, Lf, Lp, popped;
+  bool compress;
+};
+Lens lens_after_update(const sf_stream_config& c, int Lc, int Lf, int Lp, int n_chunk) {
+  Lens r{Lc, Lf + n_chunk, Lp - n_chunk, 0, false};
+  if (r.Lf > c.fifo_len) {
+    r.popped = std::min(r.Lf, std::max(c.update_period, r.Lf - c.fifo_len));
+    r.Lc += r.popped;
+    r.Lf -= r.popped;
+  }
+  if (r.Lc > c.spkcache_len) {
+    r.compress = true;
+    r.Lc = c.spkcache_len;
+  }
+  return r;
 }
 
 void reset_device(sf_stream* st, hipStream_t s) {
@@ -94,24 +117,22 @@ void reset_device(sf_stream* st, hipStream_t s) {
 // FIFO refresh/append, pop with silence statistics, compression.
 void state_update(sf_stream* st, const float* probs, int W, int n_chunk, hipStream_t s) {
   const int S = st->S, D = st->D, B = st->B, cap = st->cap, cur = st->cur;
+  const Lens n = lens_after_update(st->sc, st->Lc, st->Lf, st->Lp, n_chunk);
   refresh_probs(probs, W, S, B, st->Lc, st->Lf + n_chunk, st->P[cur], st->ph[cur], cap, s);
-  st->Lf += n_chunk;
-  st->Lp -= n_chunk;
-  if (st->Lf > st->sc.fifo_len) {
-    const int np = std::min(st->Lf, std::max(st->sc.update_period, st->Lf - st->sc.fifo_len));
-    silence_update(st->E[cur], st->P[cur], cap, D, S, B, st->Lc, np, st->sil_sum, st->sil_cnt, s);
-    st->Lc += np;
-    st->Lf -= np;
-  }
-  if (st->Lc > st->sc.spkcache_len) {
+  if (n.popped > 0)
+    silence_update(st->E[cur], st->P[cur], cap, D, S, B, st->Lc, n.popped, st->sil_sum,
+                   st->sil_cnt, s);
+  if (n.compress) {
     const int C = st->sc.spkcache_len, per = C / S;
     const int k = std::max(0, per - st->sc.n_sil_per_spk);
-    compress_cache(st->E[cur], st->P[cur], st->ph[cur], cap, D, S, B, st->Lc, st->Lf + st->Lp,
-                   st->sil_sum, st->sil_cnt, C, per, k, st->E[cur ^ 1], st->P[cur ^ 1],
-                   st->ph[cur ^ 1], st->slots, s);
+    compress_cache(st->E[cur], st->P[cur], st->ph[cur], cap, D, S, B, st->Lc + n.popped,
+                   n.Lf + n.Lp, st->sil_sum, st->sil_cnt, C, per, k, st->E[cur ^ 1],
+                   st->P[cur ^ 1], st->ph[cur ^ 1], st->slots, s);
     st->cur ^= 1;
-    st->Lc = C;
   }
+  st->Lc = n.Lc;
+  st->Lf = n.Lf;
+  st->Lp = n.Lp;
 }
 
 // Releases the cached graphs. A replay may still be queued on any stream the
@@ -251,6 +272,30 @@ void sortformer_free(sf_model* m) { delete m; }
 sf_status sortformer_get_config(const sf_model* m, sf_model_config* out) {
   if (!m || !out) return SF_EINVAL;
   *out = m->cfg;
+  return SF_OK;
+}
+
+sf_status sortformer_get_metadata(const sf_model* m, sf_model_metadata* out) {
+  if (!m || !out) return SF_EINVAL;
+  const bool sfm_ = m->cfg.arch == SF_ARCH_SORTFORMER;
+  sf_model_metadata d{};
+  d.window_stride = 0.01;
+  d.output_frame_s = sfm_ ? 0.08 : 0.01;
+  d.sample_rate = 16000;
+  d.subsampling_factor = 8;
+  d.fc_d_model = sfm_ ? 512 : 0;
+  d.tf_d_model = sfm_ ? 192 : 512;
+  d.max_num_of_spks = m->cfg.n_spk;
+  d.spkcache_len = 188;
+  d.n_mels = 128;
+  d.n_fft = 512;
+  d.win_length = 400;
+  d.hop_length = 160;
+  d.n_conformer_layers = sfm_ ? 17 : 0;
+  d.n_transformer_layers = sfm_ ? 18 : 31;
+  d.n_heads = 8;
+  d.max_window = SF_MAX_WINDOW;
+  *out = d;
   return SF_OK;
 }
 
@@ -449,58 +494,127 @@ int32_t sortformer_stream_max_emit(const sf_stream* st) {
   return st->m->cfg.arch == SF_ARCH_NEMOTRON ? 8 * n : n;
 }
 
-sf_status sortformer_stream_step(sf_stream* st, const float* d_audio_new, int64_t n_new,
-                                 int32_t is_last, float* d_probs_out, int32_t* n_emitted,
-                                 void* d_ws, size_t ws_bytes, void* stream) {
-  if (!st || !n_emitted || !d_ws || !d_probs_out) return SF_EINVAL;
-  if (st->finished) return SF_ESTATE;
-  const long long need = sortformer_stream_samples_needed(st);
-  if (n_new < 0 || n_new > need || (!is_last && n_new != need)) return SF_ESHAPE;
-  if (n_new > 0 && !d_audio_new) return SF_EINVAL;
-  if (ws_bytes < stream_ws_bytes(st->m, &st->sc, st->B)) return SF_ENOMEM;
-  const hipStream_t s = HS(stream);
+}  // extern "C"
+
+namespace {
+// Host arithmetic of the next step of a stream whose samples [recv, recv +
+// n_new) are (or are about to be) in the audio ring: the encoder frames it
+// pre-encodes (up to e1), the rows it scores (n_chunk) and its window W. The
+// non-final step s covers frames up to (s+1)*chunk_len + right_context; the
+// final one scores every remaining frame of the clip with no look-ahead
+// (Transformers docs "Nemotron 3 Diarization", streaming usage). Returns false
+// when the counters are inconsistent or the window would not fit the state.
+struct StepPlan {
+  long long N;
+  int e1, n_chunk, W;
+};
+bool plan_step(const sf_stream* st, long long n_new, bool is_last, StepPlan* p) {
   const int L = st->sc.chunk_len, R = st->sc.right_context;
-  const long long N = st->recv + n_new;
-  const int T = (int)(N / 160);
-  const int e1 = is_last ? frames_of(N) : (int)((st->steps + 1) * L + R);
-  const int n_chunk = is_last ? e1 - (int)st->emitted : L;
-  const bool nm = st->m->cfg.arch == SF_ARCH_NEMOTRON;
-  *n_emitted = nm ? 8 * n_chunk : n_chunk;
-  char* p = static_cast<char*>(d_ws);
-  EncWs enc = carve_enc(st->m, p, st->B, st->cap);
-  char* pre = p + al256(enc_ws_bytes(st->m, st->B, st->cap));
-  ring_write(d_audio_new, n_new, st->B, st->ring, st->ring_cap, st->recv, s);
-  pre_encode_range(st->m, st->ring, st->ring_cap, st->ring_cap - 1, N, T, st->enc_done, e1, st->B,
-                   st->E[st->cur] + (size_t)(st->Lc + st->Lf + st->Lp) * st->D,
+  p->N = st->recv + n_new;
+  const long long e1 = is_last ? frames_of(p->N) : (st->steps + 1) * L + R;
+  if (e1 > INT_MAX / 2 || e1 < st->enc_done) return false;
+  p->e1 = (int)e1;
+  const long long n_chunk = is_last ? e1 - st->emitted : L;
+  const int fresh = p->e1 - st->enc_done;
+  if (n_chunk < 0 || n_chunk > st->Lp + fresh) return false;
+  p->n_chunk = (int)n_chunk;
+  p->W = st->Lc + st->Lf + st->Lp + fresh;
+  return p->W <= st->cap;
+}
+
+// One step whose new samples are already in the ring: pre-encode the new
+// frames into the look-ahead rows, run the window, emit the chunk rows to
+// out (row stride S, batch stride out_bstride floats) and update the cache.
+// graphs: the window forward may run from a captured graph (stream option).
+void step_from_ring(sf_stream* st, const StepPlan& p, bool is_last, float* out,
+                    long long out_bstride, void* d_ws, hipStream_t s, bool graphs = true) {
+  char* ws = static_cast<char*>(d_ws);
+  EncWs enc = carve_enc(st->m, ws, st->B, st->cap);
+  char* pre = ws + al256(enc_ws_bytes(st->m, st->B, st->cap));
+  const int T = (int)(p.N / 160);
+  pre_encode_range(st->m, st->ring, st->ring_cap, st->ring_cap - 1, p.N, T, st->enc_done, p.e1,
+                   st->B, st->E[st->cur] + (size_t)(st->Lc + st->Lf + st->Lp) * st->D,
                    (long long)st->cap * st->D, pre, s);
-  st->Lp += e1 - st->enc_done;
-  st->enc_done = e1;
-  st->recv = N;
-  if (n_chunk > 0)
-    step_core(st, n_chunk, d_probs_out, (long long)(*n_emitted) * st->S, enc, d_ws, s);
+  st->Lp += p.e1 - st->enc_done;
+  st->enc_done = p.e1;
+  st->recv = p.N;
+  if (p.n_chunk > 0) step_core(st, p.n_chunk, out, out_bstride, enc, graphs ? d_ws : nullptr, s);
   st->steps += 1;
-  st->emitted += n_chunk;
-  st->finished = is_last != 0;
-  return launched();
+  st->emitted += p.n_chunk;
+  st->finished = is_last;
 }
 
-sf_status sortformer_stream_get_info(const sf_stream* st, int64_t* info, void** ptrs) {
-  if (!st) return SF_EINVAL;
-  if (info) {
-    info[0] = st->Lc; info[1] = st->Lf; info[2] = st->Lp; info[3] = st->cap;
-    info[4] = st->steps; info[5] = st->emitted; info[6] = st->recv; info[7] = st->finished;
+int emit_rate(const sf_stream* st) { return st->m->cfg.arch == SF_ARCH_NEMOTRON ? 8 : 1; }
+
+// The steps a feed of n_new more samples runs, on a copy of the counters: the
+// non-final steps whose audio is complete, then (is_last) the final step.
+// Returns false if any of them would be refused.
+bool plan_feed(const sf_stream* st0, long long n_new, bool is_last, long long* frames,
+               int* n_steps) {
+  sf_stream st = *st0;  // host counters only; no device work
+  st.graphs.clear();
+  long long avail = st.pending + n_new, out = 0;
+  int k = 0;
+  while (!st.finished) {
+    const long long need = sortformer_stream_samples_needed(&st);
+    const bool full = avail >= need;
+    if (!full && !is_last) break;
+    StepPlan p;
+    if (!plan_step(&st, full ? need : avail, !full, &p)) return false;
+    const Lens n = lens_after_update(st.sc, st.Lc, st.Lf, st.Lp + p.e1 - st.enc_done, p.n_chunk);
+    st.Lc = n.Lc; st.Lf = n.Lf; st.Lp = n.Lp;
+    st.enc_done = p.e1;
+    st.recv = p.N;
+    st.steps += 1;
+    st.emitted += p.n_chunk;
+    st.finished = !full;
+    avail -= full ? need : avail;
+    out += (long long)emit_rate(&st) * p.n_chunk;
+    ++k;
   }
-  if (ptrs) {
-    ptrs[0] = st->E[st->cur]; ptrs[1] = st->P[st->cur]; ptrs[2] = st->ph[st->cur];
-    ptrs[3] = st->sil_sum; ptrs[4] = st->sil_cnt;
-    ptrs[5] = reinterpret_cast<void*>((intptr_t)st->D);
-  }
-  return SF_OK;
+  *frames = out;
+  *n_steps = k;
+  return true;
 }
 
-static sf_status copy_state(sf_stream* st, bool to_host, float* emb, float* probs, int32_t* flags,
-                            double* sum, int32_t* cnt, hipStream_t s) {
-  const int rows = st->Lc + st->Lf + st->Lp, B = st->B, D = st->D, S = st->S, cur = st->cur;
+// Checkpoint blob: a fixed header, then emb (B, rows, D) fp32, probs (B, rows,
+// S) fp32, flags (B, rows) int32, silence sums (B, D) fp64, silence counts (B)
+// int32 and the audio ring (B, ring_cap) fp32, each section 256-byte aligned
+// and sized for the capacity (rows = cache + FIFO + look-ahead rows in use,
+// stored densely at the start of their section), so every blob of a stream
+// configuration has the same size.
+constexpr uint64_t CKPT_MAGIC = 0x3130544b43464653ull;  // "SFFCKT01"
+struct CkptHeader {
+  uint64_t magic;
+  int32_t version, arch, n_spk, dim, batch, cap;
+  int32_t cfg[6];
+  int64_t ring_cap;
+  int32_t Lc, Lf, Lp, enc_done;
+  int64_t steps, emitted, recv, pending;
+  int32_t finished, rows;
+  int64_t bytes;
+};
+static_assert(sizeof(CkptHeader) <= 256, "checkpoint header");
+struct CkptLayout {
+  size_t emb, probs, flags, sum, cnt, ring, total;
+};
+CkptLayout ckpt_layout(int B, int rows, int D, int S, long long ring_cap) {
+  CkptLayout c{};
+  size_t o = 256;
+  c.emb = o; o += al256((size_t)B * rows * D * 4);
+  c.probs = o; o += al256((size_t)B * rows * S * 4);
+  c.flags = o; o += al256((size_t)B * rows * 4);
+  c.sum = o; o += al256((size_t)B * D * 8);
+  c.cnt = o; o += al256((size_t)B * 4);
+  c.ring = o; o += al256((size_t)B * ring_cap * 4);
+  c.total = o;
+  return c;
+}
+
+// Rows [0, rows) of the current state buffers <-> host (row-major, dense).
+bool copy_rows_host(sf_stream* st, bool to_host, int rows, float* emb, float* probs, int32_t* flags,
+                    double* sum, int32_t* cnt, hipStream_t s) {
+  const int B = st->B, D = st->D, S = st->S, cur = st->cur;
   const hipMemcpyKind k = to_host ? hipMemcpyDeviceToHost : hipMemcpyHostToDevice;
   auto c2 = [&](void* dev, void* host, size_t row_bytes, size_t dev_pitch) -> bool {
     if (rows == 0 || !host) return true;
@@ -518,28 +632,203 @@ static sf_status copy_state(sf_stream* st, bool to_host, float* emb, float* prob
   if (ok && cnt)
     ok = (to_host ? hipMemcpyAsync(cnt, st->sil_cnt, (size_t)B * 4, k, s)
                   : hipMemcpyAsync(st->sil_cnt, cnt, (size_t)B * 4, k, s)) == hipSuccess;
-  if (!ok || hipStreamSynchronize(s) != hipSuccess) return SF_EHIP;
+  return ok;
+}
+}  // namespace
+
+extern "C" {
+
+sf_status sortformer_stream_step(sf_stream* st, const float* d_audio_new, int64_t n_new,
+                                 int32_t is_last, float* d_probs_out, int32_t* n_emitted,
+                                 void* d_ws, size_t ws_bytes, void* stream) {
+  if (!st || !n_emitted || !d_ws || !d_probs_out) return SF_EINVAL;
+  if (st->finished || st->rows_only || st->pending != 0) return SF_ESTATE;
+  const long long need = sortformer_stream_samples_needed(st);
+  if (n_new < 0 || n_new > need || (!is_last && n_new != need)) return SF_ESHAPE;
+  if (n_new > 0 && !d_audio_new) return SF_EINVAL;
+  if (ws_bytes < stream_ws_bytes(st->m, &st->sc, st->B)) return SF_ENOMEM;
+  StepPlan p;
+  if (!plan_step(st, n_new, is_last != 0, &p)) return SF_ESTATE;
+  const hipStream_t s = HS(stream);
+  *n_emitted = emit_rate(st) * p.n_chunk;
+  ring_write(d_audio_new, n_new, n_new, st->B, st->ring, st->ring_cap, st->recv, s);
+  step_from_ring(st, p, is_last != 0, d_probs_out, (long long)(*n_emitted) * st->S, d_ws, s);
+  return launched();
+}
+
+int64_t sortformer_stream_feed_frames(const sf_stream* st, int64_t n_new, int32_t is_last) {
+  if (!st || n_new < 0 || st->rows_only) return -1;
+  if (st->finished) return n_new == 0 ? 0 : -1;
+  long long frames = 0;
+  int k = 0;
+  if (!plan_feed(st, n_new, is_last != 0, &frames, &k)) return -1;
+  return frames;
+}
+
+sf_status sortformer_stream_feed(sf_stream* st, const float* d_audio_new, int64_t n_new,
+                                 int32_t is_last, float* d_probs_out, int64_t out_frames,
+                                 int64_t* n_emitted, void* d_ws, size_t ws_bytes, void* stream) {
+  if (!st || !n_emitted || !d_ws || n_new < 0) return SF_EINVAL;
+  if (n_new > 0 && !d_audio_new) return SF_EINVAL;
+  if (st->finished || st->rows_only) return SF_ESTATE;
+  if (ws_bytes < stream_ws_bytes(st->m, &st->sc, st->B)) return SF_ENOMEM;
+  long long frames = 0;
+  int n_steps = 0;
+  if (!plan_feed(st, n_new, is_last != 0, &frames, &n_steps)) return SF_ESTATE;
+  if (frames > out_frames || (frames > 0 && !d_probs_out)) return SF_ENOMEM;
+  *n_emitted = frames;
+  const hipStream_t s = HS(stream);
+  const long long ob = out_frames * st->S;  // batch stride of the output (floats)
+  long long used = 0, e0 = 0;               // samples of d_audio_new consumed, frames emitted
+  for (int i = 0; i < n_steps; ++i) {
+    const long long need = sortformer_stream_samples_needed(st);
+    const long long take = std::min(need - st->pending, n_new - used);
+    ring_write(d_audio_new + used, n_new, take, st->B, st->ring, st->ring_cap,
+               st->recv + st->pending, s);
+    used += take;
+    const bool full = st->pending + take >= need;
+    StepPlan p;
+    plan_step(st, st->pending + take, !full, &p);  // checked by plan_feed
+    st->pending = 0;
+    step_from_ring(st, p, !full, d_probs_out + e0 * st->S, ob, d_ws, s);
+    e0 += (long long)emit_rate(st) * p.n_chunk;
+  }
+  // the rest waits in the ring for the next feed
+  ring_write(d_audio_new + used, n_new, n_new - used, st->B, st->ring, st->ring_cap,
+             st->recv + st->pending, s);
+  st->pending += n_new - used;
+  return launched();
+}
+
+sf_status sortformer_stream_get_info(const sf_stream* st, int64_t* info, void** ptrs) {
+  if (!st) return SF_EINVAL;
+  if (info) {
+    info[0] = st->Lc; info[1] = st->Lf; info[2] = st->Lp; info[3] = st->cap;
+    info[4] = st->steps; info[5] = st->emitted; info[6] = st->recv; info[7] = st->finished;
+    info[8] = st->pending;
+  }
+  if (ptrs) {
+    ptrs[0] = st->E[st->cur]; ptrs[1] = st->P[st->cur]; ptrs[2] = st->ph[st->cur];
+    ptrs[3] = st->sil_sum; ptrs[4] = st->sil_cnt;
+    ptrs[5] = reinterpret_cast<void*>((intptr_t)st->D);
+  }
   return SF_OK;
 }
 
-sf_status sortformer_stream_export(const sf_stream* st, float* emb, float* probs, int32_t* flags,
-                                   double* sum, int32_t* cnt, void* stream) {
+sf_status sortformer_stream_get_rows(const sf_stream* st, float* emb, float* probs, int32_t* flags,
+                                     double* sum, int32_t* cnt, void* stream) {
   if (!st) return SF_EINVAL;
-  return copy_state(const_cast<sf_stream*>(st), true, emb, probs, flags, sum, cnt, HS(stream));
+  sf_stream* m = const_cast<sf_stream*>(st);
+  const hipStream_t s = HS(stream);
+  if (!copy_rows_host(m, true, st->Lc + st->Lf + st->Lp, emb, probs, flags, sum, cnt, s) ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return SF_EHIP;
+  return SF_OK;
 }
 
-sf_status sortformer_stream_import(sf_stream* st, int32_t Lc, int32_t Lf, int32_t Lp,
-                                   const float* emb, const float* probs, const int32_t* flags,
-                                   const double* sum, const int32_t* cnt, void* stream) {
+sf_status sortformer_stream_set_rows(sf_stream* st, int32_t Lc, int32_t Lf, int32_t Lp,
+                                     const float* emb, const float* probs, const int32_t* flags,
+                                     const double* sum, const int32_t* cnt, void* stream) {
   if (!st) return SF_EINVAL;
   if (Lc < 0 || Lf < 0 || Lp < 0 || Lc > st->sc.spkcache_len || Lf > st->sc.fifo_len ||
       Lp > st->sc.chunk_len + st->sc.right_context)
     return SF_ESHAPE;
   if ((Lc + Lf + Lp > 0) && (!emb || !probs || !flags)) return SF_EINVAL;
+  const hipStream_t s = HS(stream);
+  if (!copy_rows_host(st, false, Lc + Lf + Lp, const_cast<float*>(emb), const_cast<float*>(probs),
+                      const_cast<int32_t*>(flags), const_cast<double*>(sum),
+                      const_cast<int32_t*>(cnt), s) ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return SF_EHIP;
   st->Lc = Lc; st->Lf = Lf; st->Lp = Lp;
-  return copy_state(st, false, const_cast<float*>(emb), const_cast<float*>(probs),
-                    const_cast<int32_t*>(flags), const_cast<double*>(sum),
-                    const_cast<int32_t*>(cnt), HS(stream));
+  st->rows_only = true;
+  return SF_OK;
+}
+
+size_t sortformer_stream_checkpoint_bytes(const sf_stream* st) {
+  if (!st) return 0;
+  return ckpt_layout(st->B, st->cap, st->D, st->S, st->ring_cap).total;
+}
+
+sf_status sortformer_stream_export(const sf_stream* st, void* host, size_t bytes, void* stream) {
+  if (!st || !host) return SF_EINVAL;
+  if (st->rows_only) return SF_ESTATE;
+  if (bytes < sortformer_stream_checkpoint_bytes(st)) return SF_ENOMEM;
+  const int rows = st->Lc + st->Lf + st->Lp;
+  const CkptLayout L = ckpt_layout(st->B, st->cap, st->D, st->S, st->ring_cap);
+  char* h = static_cast<char*>(host);
+  std::memset(h, 0, L.total);
+  CkptHeader hd{};
+  hd.magic = CKPT_MAGIC;
+  hd.version = 1;
+  hd.arch = st->m->cfg.arch; hd.n_spk = st->S; hd.dim = st->D; hd.batch = st->B; hd.cap = st->cap;
+  const sf_stream_config& c = st->sc;
+  const int32_t cfg[6] = {c.chunk_len, c.right_context, c.fifo_len, c.update_period,
+                          c.spkcache_len, c.n_sil_per_spk};
+  std::memcpy(hd.cfg, cfg, sizeof cfg);
+  hd.ring_cap = st->ring_cap;
+  hd.Lc = st->Lc; hd.Lf = st->Lf; hd.Lp = st->Lp; hd.enc_done = st->enc_done;
+  hd.steps = st->steps; hd.emitted = st->emitted; hd.recv = st->recv; hd.pending = st->pending;
+  hd.finished = st->finished; hd.rows = rows;
+  hd.bytes = (int64_t)L.total;
+  std::memcpy(h, &hd, sizeof hd);
+  sf_stream* m = const_cast<sf_stream*>(st);
+  const hipStream_t s = HS(stream);
+  bool ok = copy_rows_host(m, true, rows, reinterpret_cast<float*>(h + L.emb),
+                           reinterpret_cast<float*>(h + L.probs), reinterpret_cast<int32_t*>(h + L.flags),
+                           reinterpret_cast<double*>(h + L.sum), reinterpret_cast<int32_t*>(h + L.cnt), s);
+  ok = ok && hipMemcpyAsync(h + L.ring, st->ring, (size_t)st->B * st->ring_cap * 4,
+                            hipMemcpyDeviceToHost, s) == hipSuccess;
+  if (!ok || hipStreamSynchronize(s) != hipSuccess) return SF_EHIP;
+  return SF_OK;
+}
+
+sf_status sortformer_stream_import(sf_stream* st, const void* host, size_t bytes, void* stream) {
+  if (!st || !host || bytes < 256) return SF_EINVAL;
+  CkptHeader hd;
+  std::memcpy(&hd, host, sizeof hd);
+  const sf_stream_config& c = st->sc;
+  const int32_t cfg[6] = {c.chunk_len, c.right_context, c.fifo_len, c.update_period,
+                          c.spkcache_len, c.n_sil_per_spk};
+  if (hd.magic != CKPT_MAGIC || hd.version != 1) return SF_EINVAL;
+  if (hd.arch != st->m->cfg.arch || hd.n_spk != st->S || hd.dim != st->D || hd.batch != st->B ||
+      hd.cap != st->cap || hd.ring_cap != st->ring_cap || std::memcmp(hd.cfg, cfg, sizeof cfg) != 0)
+    return SF_EINVAL;  // another model, batch or stream configuration
+  // counters of a stream the step/feed functions produced: lengths within the
+  // configuration, the look-ahead rows are the pre-encoded frames not yet
+  // scored, cache + FIFO hold at most the scored frames, the samples held
+  // cover every pre-encoded frame and less than one step is pending
+  const bool sane =
+      hd.rows == hd.Lc + hd.Lf + hd.Lp && hd.Lc >= 0 && hd.Lf >= 0 && hd.Lp >= 0 &&
+      hd.Lc <= c.spkcache_len && hd.Lf <= c.fifo_len && hd.Lp <= c.chunk_len + c.right_context &&
+      hd.steps >= 0 && hd.emitted >= 0 && hd.recv >= 0 && hd.pending >= 0 && hd.enc_done >= 0 &&
+      (hd.finished == 0 || hd.finished == 1) && hd.emitted + hd.Lp == hd.enc_done &&
+      hd.Lc + hd.Lf <= hd.emitted && hd.enc_done <= frames_of(hd.recv) &&
+      hd.pending < 1280LL * (c.chunk_len + c.right_context) + 40 &&
+      (hd.steps > 0 || (hd.recv == 0 && hd.enc_done == 0));
+  if (!sane) return SF_EINVAL;
+  const CkptLayout L = ckpt_layout(st->B, st->cap, st->D, st->S, st->ring_cap);
+  if (hd.bytes != (int64_t)L.total || bytes < L.total) return SF_EINVAL;
+  const char* h = static_cast<const char*>(host);
+  const hipStream_t s = HS(stream);
+  reset_device(st, s);  // flags of both buffers cleared
+  st->cur = 0;
+  bool ok = copy_rows_host(st, false, hd.rows, reinterpret_cast<float*>(const_cast<char*>(h + L.emb)),
+                           reinterpret_cast<float*>(const_cast<char*>(h + L.probs)),
+                           reinterpret_cast<int32_t*>(const_cast<char*>(h + L.flags)),
+                           reinterpret_cast<double*>(const_cast<char*>(h + L.sum)),
+                           reinterpret_cast<int32_t*>(const_cast<char*>(h + L.cnt)), s);
+  ok = ok && hipMemcpyAsync(st->ring, h + L.ring, (size_t)st->B * st->ring_cap * 4,
+                            hipMemcpyHostToDevice, s) == hipSuccess;
+  if (!ok || hipStreamSynchronize(s) != hipSuccess) {
+    reset_host(st);  // never leave half-imported counters behind
+    return SF_EHIP;
+  }
+  st->Lc = hd.Lc; st->Lf = hd.Lf; st->Lp = hd.Lp; st->enc_done = hd.enc_done;
+  st->steps = hd.steps; st->emitted = hd.emitted; st->recv = hd.recv; st->pending = hd.pending;
+  st->finished = hd.finished != 0;
+  st->rows_only = false;
+  return SF_OK;
 }
 
 sf_status sortformer_stream_update(sf_stream* st, const float* d_wp, int32_t n_chunk, void* d_ws,

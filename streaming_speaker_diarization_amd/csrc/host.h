@@ -95,8 +95,11 @@ struct sf_stream {
   float* ring;
   int Lc, Lf, Lp;
   long long steps, emitted, recv;
+  long long pending;  // samples fed past recv, held in the ring for the next step
   int enc_done;
   bool finished;
+  bool rows_only;     // rows written by sortformer_stream_set_rows: steps refused until
+                      // a reset or a checkpoint import makes the counters consistent
   // window-forward graphs keyed by (window rows, ping-pong buffer, workspace)
   // (HIP handles kept opaque here: this header is also built by the host compiler)
   bool use_graphs;

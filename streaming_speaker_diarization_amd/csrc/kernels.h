@@ -128,8 +128,10 @@ void copy_rows(const float* src, long long s_bstride, int s_ld, float* dst, long
                int d_ld, int B, int rows, int cols, hipStream_t s);
 // n contiguous elements (fp32, or bf16 when src_bf16) widened to fp32
 void widen(const void* src, bool src_bf16, float* dst, long long n, hipStream_t s);
-void ring_write(const float* src, long long n_new, int B, float* ring, long long ring_cap,
-                long long start, hipStream_t s);
+// n samples of each stream (stream b's at src + b*src_bstride) into the audio
+// ring at absolute positions start .. start+n-1 (modulo the power-of-two cap)
+void ring_write(const float* src, long long src_bstride, long long n_new, int B, float* ring,
+                long long ring_cap, long long start, hipStream_t s);
 void fill_i32(int* p, long long n, int v, hipStream_t s);
 void fill_f64(double* p, long long n, double v, hipStream_t s);
 void refresh_probs(const float* win_probs, int W, int S, int B, int Lc, int nrows, float* P,

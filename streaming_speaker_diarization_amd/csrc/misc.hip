@@ -617,18 +617,18 @@ void widen(const void* src, bool src_bf16, float* dst, long long n, hipStream_t 
                      src_bf16, dst, n);
 }
 
-__global__ void ring_write_kernel(const float* src, long long n, float* ring, long long cap,
-                                  long long start) {
+__global__ void ring_write_kernel(const float* src, long long src_bstride, long long n,
+                                  float* ring, long long cap, long long start) {
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
   const int b = blockIdx.y;
-  if (i < n) ring[(size_t)b * cap + ((start + i) & (cap - 1))] = src[(size_t)b * n + i];
+  if (i < n) ring[(size_t)b * cap + ((start + i) & (cap - 1))] = src[(size_t)b * src_bstride + i];
 }
 
-void ring_write(const float* src, long long n, int B, float* ring, long long cap, long long start,
-                hipStream_t s) {
+void ring_write(const float* src, long long src_bstride, long long n, int B, float* ring,
+                long long cap, long long start, hipStream_t s) {
   if (n <= 0) return;
   hipLaunchKernelGGL(ring_write_kernel, dim3((unsigned)((n + 255) / 256), B), dim3(256), 0, s, src,
-                     n, ring, cap, start);
+                     src_bstride, n, ring, cap, start);
 }
 
 __global__ void fill_i32_kernel(int* p, long long n, int v) {

@@ -36,6 +36,9 @@ class Model:
             sf.sortformer_free(h)
             self.handle = None
 
+    def metadata(self) -> dict:
+        return sf.sortformer_get_metadata(self.handle)
+
     def workspace(self, nbytes: int) -> torch.Tensor:
         if self._ws is None or self._ws.numel() < nbytes:
             self._ws = _bytes(nbytes, self.device)
@@ -118,6 +121,27 @@ class Stream:
                                       is_last, self.out, self.ws)
         # the library writes the emitted rows densely as (B, n, S)
         return self.out.view(-1)[:self.B * n * self.model.n_spk].view(self.B, n, self.model.n_spk)
+
+    def feed(self, audio_new: torch.Tensor, is_last: bool = False) -> torch.Tensor:
+        """Any number of new samples (B, n) on the device -> the probabilities
+        (B, frames, S) of every step they completed (possibly none); the rest
+        waits in the stream's audio ring. A fresh tensor each call."""
+        n = audio_new.shape[1]
+        frames = sf.sortformer_stream_feed_frames(self.handle, n, is_last)
+        if frames < 0:
+            raise sf.SortformerError(sf.SF_ESTATE, "stream_feed")
+        out = torch.empty(self.B, max(frames, 1), self.model.n_spk, dtype=torch.float32,
+                          device=self.model.device)
+        got = sf.sortformer_stream_feed(self.handle, audio_new.contiguous(), is_last, out, self.ws)
+        return out[:, :got]
+
+    def export(self):
+        """The whole stream state (cache, FIFO, look-ahead, silence statistics,
+        audio ring, counters) as a host byte array."""
+        return sf.sortformer_stream_export(self.handle)
+
+    def import_(self, blob):
+        sf.sortformer_stream_import(self.handle, blob)
 
     def reset(self):
         sf.sortformer_stream_reset(self.handle)

@@ -27,6 +27,8 @@ EXPORTS = [
     "sortformer_stream_create", "sortformer_stream_destroy", "sortformer_stream_reset",
     "sortformer_stream_samples_needed", "sortformer_stream_max_emit", "sortformer_stream_step",
     "sortformer_stream_get_info", "sortformer_stream_export", "sortformer_stream_import",
+    "sortformer_stream_checkpoint_bytes", "sortformer_stream_get_rows", "sortformer_stream_set_rows",
+    "sortformer_stream_feed", "sortformer_stream_feed_frames", "sortformer_get_metadata",
     "sortformer_stream_update",
     "sortformer_encode_workspace_bytes", "sortformer_encode_window", "sortformer_pre_encode",
     "sortformer_pre_encode_workspace_bytes", "sortformer_config_num_tensors",
@@ -49,6 +51,17 @@ class sf_stream_config(C.Structure):
     _fields_ = [("chunk_len", C.c_int32), ("right_context", C.c_int32),
                 ("fifo_len", C.c_int32), ("update_period", C.c_int32),
                 ("spkcache_len", C.c_int32), ("n_sil_per_spk", C.c_int32)]
+
+
+class sf_model_metadata(C.Structure):
+    _fields_ = [("window_stride", C.c_double), ("output_frame_s", C.c_double),
+                ("sample_rate", C.c_int32), ("subsampling_factor", C.c_int32),
+                ("fc_d_model", C.c_int32), ("tf_d_model", C.c_int32),
+                ("max_num_of_spks", C.c_int32), ("spkcache_len", C.c_int32),
+                ("n_mels", C.c_int32), ("n_fft", C.c_int32), ("win_length", C.c_int32),
+                ("hop_length", C.c_int32), ("n_conformer_layers", C.c_int32),
+                ("n_transformer_layers", C.c_int32), ("n_heads", C.c_int32),
+                ("max_window", C.c_int32)]
 
 
 class sf_segment_params(C.Structure):
@@ -105,8 +118,14 @@ def load(path: str = LIB_PATH):
         "sortformer_stream_max_emit": (I32, [P]),
         "sortformer_stream_step": (I32, [P, P, I64, I32, P, C.POINTER(I32), P, SZ, P]),
         "sortformer_stream_get_info": (I32, [P, C.POINTER(I64), C.POINTER(P)]),
-        "sortformer_stream_export": (I32, [P, P, P, P, P, P, P]),
-        "sortformer_stream_import": (I32, [P, I32, I32, I32, P, P, P, P, P, P]),
+        "sortformer_stream_checkpoint_bytes": (SZ, [P]),
+        "sortformer_stream_export": (I32, [P, P, SZ, P]),
+        "sortformer_stream_import": (I32, [P, P, SZ, P]),
+        "sortformer_stream_get_rows": (I32, [P, P, P, P, P, P, P]),
+        "sortformer_stream_set_rows": (I32, [P, I32, I32, I32, P, P, P, P, P, P]),
+        "sortformer_stream_feed": (I32, [P, P, I64, I32, P, I64, C.POINTER(I64), P, SZ, P]),
+        "sortformer_stream_feed_frames": (I64, [P, I64, I32]),
+        "sortformer_get_metadata": (I32, [P, C.POINTER(sf_model_metadata)]),
         "sortformer_stream_update": (I32, [P, P, I32, P, SZ, P]),
         "sortformer_encode_workspace_bytes": (SZ, [P, I32, I32]),
         "sortformer_encode_window": (I32, [P, P, I32, I32, I32, P, P, P, SZ, P]),
@@ -203,6 +222,12 @@ def sortformer_init(cfg, seed, d_weights, stream=None):
 
 def sortformer_free(h):
     load().sortformer_free(h)
+
+
+def sortformer_get_metadata(h) -> dict:
+    md = sf_model_metadata()
+    _check(load().sortformer_get_metadata(h, C.byref(md)), "get_metadata")
+    return {k: getattr(md, k) for k, _ in sf_model_metadata._fields_}
 
 
 def sortformer_num_tensors(h) -> int:
@@ -311,12 +336,29 @@ def sortformer_stream_step(st, d_audio_new, n_new, is_last, d_probs_out, d_ws, s
     return n.value
 
 
+def sortformer_stream_feed_frames(st, n_new, is_last=False) -> int:
+    return load().sortformer_stream_feed_frames(st, n_new, int(is_last))
+
+
+def sortformer_stream_feed(st, d_audio_new, is_last, d_probs_out, d_ws, stream=None) -> int:
+    """Feed d_audio_new (B, n) (any n) -> frames per stream written to d_probs_out
+    (B, out_frames, S), row 0 onwards."""
+    B, S = _STREAMS[st.value]
+    n_new = d_audio_new.shape[1]
+    out_frames = d_probs_out.shape[1]
+    n = C.c_int64()
+    _check(load().sortformer_stream_feed(st, _ptr(d_audio_new, B * n_new), n_new, int(is_last),
+                                         _ptr(d_probs_out, B * out_frames * S), out_frames,
+                                         C.byref(n), *_buf(d_ws), _stream(stream)), "stream_feed")
+    return n.value
+
+
 def sortformer_stream_get_info(st):
-    info = (C.c_int64 * 8)()
+    info = (C.c_int64 * 9)()
     ptrs = (C.c_void_p * 6)()
     _check(load().sortformer_stream_get_info(st, info, ptrs), "stream_get_info")
     keys = ["cache_len", "fifo_len", "lookahead_len", "capacity", "steps", "frames_emitted",
-            "samples_received", "finished"]
+            "samples_received", "finished", "pending"]
     return dict(zip(keys, list(info))), [p or 0 for p in ptrs]
 
 
@@ -324,7 +366,27 @@ def _np(a):
     return None if a is None else a.ctypes.data_as(C.c_void_p)
 
 
-def sortformer_stream_export(st, n_spk, stream=None):
+def sortformer_stream_checkpoint_bytes(st) -> int:
+    return load().sortformer_stream_checkpoint_bytes(st)
+
+
+def sortformer_stream_export(st, stream=None):
+    """-> the whole streaming state as a host byte array (numpy uint8)."""
+    import numpy as np
+    blob = np.zeros(sortformer_stream_checkpoint_bytes(st), np.uint8)
+    _check(load().sortformer_stream_export(st, _np(blob), blob.nbytes, _stream(stream)),
+           "stream_export")
+    return blob
+
+
+def sortformer_stream_import(st, blob, stream=None):
+    import numpy as np
+    blob = np.ascontiguousarray(blob, np.uint8)
+    _check(load().sortformer_stream_import(st, _np(blob), blob.nbytes, _stream(stream)),
+           "stream_import")
+
+
+def sortformer_stream_get_rows(st, n_spk, stream=None):
     """-> dict of host arrays (emb, probs, flags, sil_sum, sil_cnt) and lengths."""
     import numpy as np
     info, ptrs = sortformer_stream_get_info(st)
@@ -334,22 +396,22 @@ def sortformer_stream_export(st, n_spk, stream=None):
     out = dict(emb=np.empty((B, rows, D), np.float32), probs=np.empty((B, rows, n_spk), np.float32),
                flags=np.empty((B, rows), np.int32), sil_sum=np.empty((B, D), np.float64),
                sil_cnt=np.empty(B, np.int32))
-    _check(load().sortformer_stream_export(st, _np(out["emb"]), _np(out["probs"]),
-                                           _np(out["flags"]), _np(out["sil_sum"]),
-                                           _np(out["sil_cnt"]), _stream(stream)), "stream_export")
+    _check(load().sortformer_stream_get_rows(st, _np(out["emb"]), _np(out["probs"]),
+                                             _np(out["flags"]), _np(out["sil_sum"]),
+                                             _np(out["sil_cnt"]), _stream(stream)), "stream_get_rows")
     out.update(info)
     return out
 
 
-def sortformer_stream_import(st, cache_len, fifo_len, lookahead_len, emb, probs, flags, sil_sum,
-                             sil_cnt, stream=None):
+def sortformer_stream_set_rows(st, cache_len, fifo_len, lookahead_len, emb, probs, flags, sil_sum,
+                               sil_cnt, stream=None):
     import numpy as np
     arrs = [np.ascontiguousarray(emb, np.float32), np.ascontiguousarray(probs, np.float32),
             np.ascontiguousarray(flags, np.int32), np.ascontiguousarray(sil_sum, np.float64),
             np.ascontiguousarray(sil_cnt, np.int32)]
-    _check(load().sortformer_stream_import(st, cache_len, fifo_len, lookahead_len,
-                                           *[_np(a) for a in arrs], _stream(stream)),
-           "stream_import")
+    _check(load().sortformer_stream_set_rows(st, cache_len, fifo_len, lookahead_len,
+                                             *[_np(a) for a in arrs], _stream(stream)),
+           "stream_set_rows")
 
 
 _STREAMS = {}  # stream handle -> (batch, speakers)

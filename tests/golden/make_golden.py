@@ -3,7 +3,8 @@
 Calls only the oracle (and the shared synthetic-input generator); the GPU
 path never writes these files. Run from the repository root:
     python tests/golden/make_golden.py [name ...]
-Outputs float32 .npy files next to this script.
+Outputs float32 .npy files (and, for the 64-stream workload, one .npz per
+kept stream) next to this script.
 """
 import os
 import sys
@@ -14,7 +15,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
 sys.path.insert(0, ROOT)
 
-from oracle import run, streaming  # noqa: E402
+from oracle import frontend, run, streaming  # noqa: E402
 from oracle.weights import make_weights  # noqa: E402
 from synthetic import workload_audio  # noqa: E402
 
@@ -40,13 +41,69 @@ def nemotron1800s():
     return p
 
 
+# 64 x 120 s ultra-low workload: the streams kept, and the steps at which the
+# oracle's window is recorded for state-forced parity (the first compression,
+# a later one's neighbourhood, the final step)
+ULTRALOW_STREAMS = (0, 9, 18, 27, 36, 45, 54, 63)
+ULTRALOW_SNAP_STEPS = (110, 300, 499)
+
+
+def ultralow_stream(b):
+    """One stream of the 64 x 120 s workload through the live 'ultra low'
+    schedule: its emitted probabilities, and at each snapshot step the window
+    the oracle encodes, stored as the pre-encoded frame index of every row
+    (-1 for a silence placeholder) with the placeholder embedding, plus the
+    oracle's probabilities over that window."""
+    w = make_weights("sortformer", 0, bf16=True)
+    audio = workload_audio("ultralow64x120s", stream=b)
+    emb = run.pre_encode_all(w, frontend.log_mel(audio))
+    cfg = streaming.StreamConfig.preset("ultra_low")
+    sched = streaming.live_schedule(len(audio), cfg)
+    index = {emb[i].tobytes(): i for i in range(len(emb))}
+    assert len(index) == len(emb)
+    base = run.sortformer_encoder(w)
+    snap, cur = {}, {}
+
+    def on_step(si, st):
+        cur.clear()
+        if si not in ULTRALOW_SNAP_STEPS:
+            return
+        rows = [-1 if ph else index[r.tobytes()] for r, ph in zip(st.cache_emb, st.cache_ph)]
+        rows += [index[r.tobytes()] for r in st.fifo_emb]
+        c0, n, rc, _ = sched[si]
+        rows += list(range(c0, c0 + n + rc))
+        phv = st.cache_emb[np.argmax(st.cache_ph)] if st.cache_ph.any() else np.zeros(emb.shape[1])
+        cur.update(step=si, rows=np.array(rows, np.int32), ph=np.asarray(phv, np.float64))
+
+    def enc(window):
+        p80, pout = base(window)
+        if cur:
+            rows = cur["rows"]
+            rebuilt = np.where(rows[:, None] >= 0, emb[np.maximum(rows, 0)], cur["ph"][None, :])
+            assert np.array_equal(rebuilt, window), "window reconstruction"
+            snap[cur["step"]] = (rows, cur["ph"], p80.astype(np.float32))
+        return p80, pout
+
+    probs, _ = streaming.run_stream(emb, cfg, enc, 4, on_step=on_step, sched=sched)
+    out = {"probs": probs.astype(np.float32)}
+    for k, (rows, ph, p) in snap.items():
+        out[f"rows_{k}"], out[f"ph_{k}"], out[f"wprobs_{k}"] = rows, ph, p
+    return out
+
+
 JOBS = {"low60s_bf16": low60s, "veryhigh600s_bf16": veryhigh600s,
         "nemotron1800s_bf16": nemotron1800s}
+JOBS.update({f"ultralow64x120s_b{b}": (lambda b=b: ultralow_stream(b)) for b in ULTRALOW_STREAMS})
 
 if __name__ == "__main__":
     names = sys.argv[1:] or list(JOBS)
     for n in names:
         t = time.time()
-        p = JOBS[n]().astype(np.float32)
-        np.save(os.path.join(HERE, n + ".npy"), p)
-        print(f"{n}: {p.shape} in {time.time() - t:.1f} s", flush=True)
+        r = JOBS[n]()
+        if isinstance(r, dict):
+            np.savez(os.path.join(HERE, n + ".npz"), **r)
+            print(f"{n}: {sorted(r)} in {time.time() - t:.1f} s", flush=True)
+        else:
+            p = r.astype(np.float32)
+            np.save(os.path.join(HERE, n + ".npy"), p)
+            print(f"{n}: {p.shape} in {time.time() - t:.1f} s", flush=True)

@@ -97,11 +97,11 @@ def test_cache_update_bit_exact(rt, sf, sfbf, nmbf, case):
     st = model.stream(preset, batch=B)
     cfg = OST.StreamConfig.preset(preset)
     emb, probs, flags, sil_sum, sil_cnt, wprobs = _random_state(B, Lc, Lf, Lp, S, 11, kind, 5)
-    sf.sortformer_stream_import(st.handle, Lc, Lf, Lp, emb, probs, flags, sil_sum, sil_cnt)
-    back = sf.sortformer_stream_export(st.handle, S)
+    sf.sortformer_stream_set_rows(st.handle, Lc, Lf, Lp, emb, probs, flags, sil_sum, sil_cnt)
+    back = sf.sortformer_stream_get_rows(st.handle, S)
     assert np.array_equal(back["emb"], emb) and np.array_equal(back["probs"], probs)
     sf.sortformer_stream_update(st.handle, _cuda(wprobs), n_chunk, st.ws)
-    got = sf.sortformer_stream_export(st.handle, S)
+    got = sf.sortformer_stream_get_rows(st.handle, S)
     for b in range(B):
         o = OST.State(emb[b, :Lc].copy(), probs[b, :Lc].copy(), flags[b, :Lc].astype(bool),
                       emb[b, Lc:Lc + Lf].copy(), probs[b, Lc:Lc + Lf].copy(), sil_sum[b].copy(),

@@ -94,3 +94,16 @@ def test_high_preset(sfbf, wbf):
     ref, _ = OR.sortformer_stream(audio, wbf, cfg, live=True)
     assert got.shape == ref.shape
     _check("high 22.3 s", got, ref)
+
+
+def test_very_high_tails_all_remainders(sfbf, wbf):
+    """'very high' (340 + 40 frames per step): clips of 3200-3215 mel frames
+    give one full step and a final step of 60-62 frames, over all 16 mel-frame
+    remainders."""
+    cfg = OST.StreamConfig.preset("very_high")
+    for r in range(16):
+        audio, T = _clip(r, 200, 1100 + r)
+        got = sfbf.stream("very_high").run(_cuda(audio)[None])[0].cpu().numpy()
+        ref, _ = OR.sortformer_stream(audio, wbf, cfg, live=True)
+        assert got.shape == ref.shape == ((T + 7) // 8, 4), r
+        _check(f"very_high tail T={T} N={len(audio)}", got, ref)
