@@ -293,15 +293,30 @@ def pmc_summary(name, fetch_dir, write_dir, copy_dir):
     fe, wr = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
 
     def is_gemm(k):
-        return k.startswith(("gemm_", "splitk_epi", "tf_tail"))
+        n = k.split("(")[0].replace("void ", "").replace("sf::", "")
+        # the fp32 relative-position table GEMM and its split-K reduction run
+        # once while the model initialises, before the probed windows
+        init = n.startswith("gemm_slice_kernel<float") or n.startswith("splitk_epi")
+        return n.startswith(("gemm_", "splitk_epi", "tf_tail")) and not init
 
     n = sum(v[0] for k, v in fe.items() if is_gemm(k))
     rd = sum(v[1] for k, v in fe.items() if is_gemm(k)) * 1024 * f_scale / max(n, 1)
     wt = sum(v[1] for k, v in wr.items() if is_gemm(k)) * 1024 * w_scale / max(n, 1)
     wl = WORKLOADS[name]
+    W = {"ultralow64x120s": 380, "low60s": 387, "veryhigh600s": 608}.get(name, 380)
+    wk = "" if name == "ultralow64x120s" else f" --workload {name}"
     lines = [f"# GEMM kernel class: HBM traffic from FETCH_SIZE / WRITE_SIZE counters", "",
              f"Workload: {name} ({wl['desc']}); counters taken on the encoder window probe",
-             "(bench.py --window-probe), one steady-state window per stream encoded twice.", "",
+             f"(bench.py --window-probe {W}): one steady-state window of {W} frames per stream, "
+             f"{wl['batch']} streams, encoded twice.", "",
+             "Commands (from /tmp, TMPDIR=/tmp; R = repository root):",
+             f"  timeout -s KILL 240 rocprofv3 --pmc FETCH_SIZE -f csv -d FETCH -o run -- python3 R/bench.py{wk} --window-probe {W}",
+             f"  timeout -s KILL 240 rocprofv3 --pmc WRITE_SIZE -f csv -d WRITE -o run -- python3 R/bench.py{wk} --window-probe {W}",
+             "  timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE -f csv -d COPY/copy_fetch -o run -- python3 R/bench.py --copy-probe 1024",
+             "  timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE -f csv -d COPY/copy_write -o run -- python3 R/bench.py --copy-probe 1024",
+             f"  python3 R/bench.py{wk} --pmc-summary FETCH WRITE COPY", "",
+             "GEMM class: every gemm_*, splitk_epi and tf_tail dispatch of the probed windows (the",
+             "relative-position table GEMM and its reduction, run once at model initialisation, excluded).", "",
              f"Calibration (1 GiB device copy {ck[0]}): FETCH_SIZE scale {f_scale:.4f}, "
              f"WRITE_SIZE scale {w_scale:.4f}", "",
              "Per kernel (KiB per dispatch, raw counter values):",
