@@ -242,6 +242,25 @@ sf_status sortformer_stream_step(sf_stream* st, const float* d_audio_new, int64_
  * make the step's window exceed the state's capacity; SF_ESHAPE for a wrong
  * n_new; SF_ENOMEM for a small workspace. */
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * step as sortformer_stream_step, with its workspace taken from a static
+ * device array of SF_NOALLOC_SCRATCH_BYTES that the library holds on every
+ * GPU it runs on until the process ends, instead of a caller buffer. The
+ * window forward is launched kernel by kernel (no graph capture, whose
+ * instantiation may allocate), and the call makes no allocation of any kind.
+ * Results are bit-identical to sortformer_stream_step's. Streams whose step
+ * workspace (sortformer_stream_workspace_bytes) exceeds the scratch size get
+ * SF_ENOMEM before any work; this covers a single stream of every preset but
+ * "very_high" and "nemotron_offline", and small batches. All calls on one GPU
+ * share its scratch array: calls that may overlap on one GPU (different host
+ * threads or different HIP streams without ordering between them) race and
+ * must be serialised by the caller. Other errors as sortformer_stream_step. */
+#define SF_NOALLOC_SCRATCH_BYTES (64ull << 20)
+sf_status sortformer_stream_step_noalloc(sf_stream* st, const float* d_audio_new, int64_t n_new,
+                                         int32_t is_last, float* d_probs_out,
+                                         int32_t* n_emitted_host, void* stream);
+
 /* Streaming feed of any sample count (the runner's "streaming feed, reset,
  * and final-flush", ExecuTorch issue, Proposed scope; the Transformers
  * streaming loop, which hands the processor audio as it arrives): the n_new

@@ -8,6 +8,7 @@
 #include <climits>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "kernels.h"
@@ -697,6 +698,56 @@ sf_status sortformer_stream_feed(sf_stream* st, const float* d_audio_new, int64_
   ring_write(d_audio_new + used, n_new, n_new - used, st->B, st->ring, st->ring_cap,
              st->recv + st->pending, s);
   st->pending += n_new - used;
+  return launched();
+}
+
+}  // extern "C"
+
+namespace {
+// Step workspace for callers that cannot allocate: one static device array per
+// GPU, of SF_NOALLOC_SCRATCH_BYTES, alive until the process ends. Its address
+// on each device is taken once, with that device current; host code uses only
+// that address (the array's own name is a host-side stand-in).
+static __device__ __align__(256) char scratch[SF_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+sf_status scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SF_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return SF_EHIP;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return SF_OK;
+}
+}  // namespace
+
+extern "C" {
+
+sf_status sortformer_stream_step_noalloc(sf_stream* st, const float* d_audio_new, int64_t n_new,
+                                         int32_t is_last, float* d_probs_out,
+                                         int32_t* n_emitted, void* stream) {
+  if (!st || !n_emitted || !d_probs_out) return SF_EINVAL;
+  if (st->finished || st->rows_only || st->pending != 0) return SF_ESTATE;
+  const long long need = sortformer_stream_samples_needed(st);
+  if (n_new < 0 || n_new > need || (!is_last && n_new != need)) return SF_ESHAPE;
+  if (n_new > 0 && !d_audio_new) return SF_EINVAL;
+  const size_t ws_bytes = stream_ws_bytes(st->m, &st->sc, st->B);
+  if (ws_bytes > SF_NOALLOC_SCRATCH_BYTES) return SF_ENOMEM;  // beyond the static scratch
+  StepPlan p;
+  if (!plan_step(st, n_new, is_last != 0, &p)) return SF_ESTATE;
+  void* ws = nullptr;
+  const sf_status got = scratch_on_current_device(&ws);
+  if (got != SF_OK) return got;
+  const hipStream_t s = HS(stream);
+  *n_emitted = emit_rate(st) * p.n_chunk;
+  ring_write(d_audio_new, n_new, n_new, st->B, st->ring, st->ring_cap, st->recv, s);
+  step_from_ring(st, p, is_last != 0, d_probs_out, (long long)(*n_emitted) * st->S, ws, s, false);
   return launched();
 }
 

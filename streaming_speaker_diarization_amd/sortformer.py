@@ -29,6 +29,7 @@ EXPORTS = [
     "sortformer_stream_get_info", "sortformer_stream_export", "sortformer_stream_import",
     "sortformer_stream_checkpoint_bytes", "sortformer_stream_get_rows", "sortformer_stream_set_rows",
     "sortformer_stream_feed", "sortformer_stream_feed_frames", "sortformer_get_metadata",
+    "sortformer_stream_step_noalloc",
     "sortformer_stream_update",
     "sortformer_encode_workspace_bytes", "sortformer_encode_window", "sortformer_pre_encode",
     "sortformer_pre_encode_workspace_bytes", "sortformer_config_num_tensors",
@@ -37,6 +38,7 @@ EXPORTS = [
     "sortformer_segments", "sortformer_debug_tap",
 ]
 SF_STREAM_OPT_GRAPHS = 1
+SF_NOALLOC_SCRATCH_BYTES = 64 << 20
 SF_TAP_LAYER_IN, SF_TAP_ATTN_CTX, SF_TAP_LAYER_OUT = 0, 1, 2
 SF_MAX_TAPS = 16
 SF_PROF = {"gemm": 1, "attn": 2, "ln": 3, "conv": 4, "frontend": 5, "cache": 6}
@@ -125,6 +127,7 @@ def load(path: str = LIB_PATH):
         "sortformer_stream_set_rows": (I32, [P, I32, I32, I32, P, P, P, P, P, P]),
         "sortformer_stream_feed": (I32, [P, P, I64, I32, P, I64, C.POINTER(I64), P, SZ, P]),
         "sortformer_stream_feed_frames": (I64, [P, I64, I32]),
+        "sortformer_stream_step_noalloc": (I32, [P, P, I64, I32, P, C.POINTER(I32), P]),
         "sortformer_get_metadata": (I32, [P, C.POINTER(sf_model_metadata)]),
         "sortformer_stream_update": (I32, [P, P, I32, P, SZ, P]),
         "sortformer_encode_workspace_bytes": (SZ, [P, I32, I32]),
@@ -333,6 +336,17 @@ def sortformer_stream_step(st, d_audio_new, n_new, is_last, d_probs_out, d_ws, s
                                          _ptr(d_probs_out, B * sortformer_stream_max_emit(st) * S),
                                          C.byref(n), *_buf(d_ws),
                                          _stream(stream)), "stream_step")
+    return n.value
+
+
+def sortformer_stream_step_noalloc(st, d_audio_new, n_new, is_last, d_probs_out, stream=None) -> int:
+    """sortformer_stream_step with the library's static scratch as workspace."""
+    n = C.c_int32()
+    B, S = _STREAMS[st.value]
+    _check(load().sortformer_stream_step_noalloc(
+        st, _ptr(d_audio_new, B * n_new), n_new, int(is_last),
+        _ptr(d_probs_out, B * sortformer_stream_max_emit(st) * S), C.byref(n), _stream(stream)),
+        "stream_step_noalloc")
     return n.value
 
 
