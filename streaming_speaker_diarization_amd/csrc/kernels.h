@@ -103,6 +103,19 @@ struct TfTailArgs {
 };
 int tf_tail(const TfTailArgs& a, hipStream_t s);
 
+// The same layer tail for batched windows (more than 4096 rows), with the FFN
+// output projection and LN2 in the kernel as well:
+//   x1 = LN1(x + ctx Wo^T + bo); xo = LN2(x1 + relu(x1 W1^T + b1) W2^T + b2)
+// and h = bf16(xo), the next layer's GEMM operand. xo may alias x (each
+// workgroup reads its rows before writing them). wo, w1, w2 fragment-major.
+struct TfLayerArgs {
+  const void* ctx; const float* x; float* xo; void* h; int M;
+  const void* wo; const float* bo; const float* g1; const float* be1;
+  const void* w1; const float* b1; const void* w2; const float* b2;
+  const float* g2; const float* be2;
+};
+void tf_layer_tp(const TfLayerArgs& a, hipStream_t s);
+
 void dwconv_time(const float* glu, int B, int W, int n_valid, const float* w9,
                  const float* scale, const float* shift, void* out, bool bf16, hipStream_t s);
 

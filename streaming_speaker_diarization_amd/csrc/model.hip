@@ -703,6 +703,13 @@ static void encode_sortformer(const sf_model* m, EncWs& w, int B, int W, int n_v
       n.part = w.part; n.nsplit = nc; n.pbias = L.b2; n.alpha = 1.f;
       n.g1 = L.ln2_g; n.b1 = L.ln2_b; n.x_mode = 2; n.y_act = w.h;
       layernorm(n, bf, s);
+    } else if (bf) {
+      // batched windows: the whole tail in one kernel
+      TfLayerArgs t{};
+      t.ctx = w.ctx; t.x = w.x; t.xo = w.x; t.h = w.h; t.M = B * W;
+      t.wo = L.wo_f; t.bo = L.bo; t.g1 = L.ln1_g; t.be1 = L.ln1_b;
+      t.w1 = L.w1_f; t.b1 = L.b1; t.w2 = L.w2_f; t.b2 = L.b2; t.g2 = L.ln2_g; t.be2 = L.ln2_b;
+      tf_layer_tp(t, s);
     } else {
       int ns = c.branch(w.ctx, 192, L.wo, 192, 192);
       c.ln(192, ns, L.bo, 1.f, L.ln1_g, L.ln1_b, nullptr, nullptr, 2, w.h);   // post-LN

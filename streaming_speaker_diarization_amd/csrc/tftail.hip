@@ -176,6 +176,233 @@ __global__ __launch_bounds__(NW * 64) void tf_tail_kernel(TfTailArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Throughput form (batched windows, more than 4096 rows): the whole layer tail
+//   x1 = LN1(x + ctx Wo^T + bo),  x <- LN2(x1 + relu(x1 W1^T + b1) W2^T + b2)
+// in one kernel, h <- x as the next GEMM operand (bf16). One workgroup = 64
+// rows; wave w owns output columns 48w .. 48w+47 of every 192-wide product
+// (3 tiles x 4 row tiles, so each weight fragment it loads feeds 4 products)
+// and, in each of the 4 hidden chunks of 192, hidden columns 48w .. 48w+47.
+// The A operands (ctx, then x1, and each hidden chunk) sit in LDS as bf16 for
+// all four waves; row statistics of both LayerNorms are reduced across the
+// waves through LDS. The output projection of the hidden layer accumulates
+// over the chunks in registers, so no partial sums leave the kernel.
+namespace {
+constexpr int TB_RB = 64, TB_NW = 4, TB_CT = 3, TB_RT = TB_RB / 16, TB_NK = TD / 32;
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void tf_layer_tp_kernel(TfLayerArgs a) {
+  using M_ = MF<bf16_t>;
+  __shared__ __align__(16) bf16_t As[TB_RB * TLH];  // ctx rows, then x1 (bf16)
+  __shared__ __align__(16) bf16_t Hs[TB_RB * TLH];  // one hidden chunk (bf16)
+  __shared__ float red[TB_NW][TB_RB];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int r0 = blockIdx.x * TB_RB;
+  auto frag = [&](const void* m, int K, int t, int s) {
+    return *reinterpret_cast<const bf16x8_t*>(static_cast<const bf16_t*>(m) +
+                                              ((size_t)t * (K / 32) + s) * 512 + 8 * lane);
+  };
+  // ---- ctx rows into LDS (16-byte chunks, rows past M clamped)
+  {
+    const bf16_t* ctx = static_cast<const bf16_t*>(a.ctx);
+    constexpr int CPR = TD / 8;  // 24 chunks per row
+#pragma unroll
+    for (int i = 0; i < TB_RB * CPR / 256; ++i) {
+      const int c = tid + 256 * i, r = c / CPR, q = c % CPR;
+      const int row = min(r0 + r, a.M - 1);
+      *reinterpret_cast<vec16*>(&As[r * TLH + 8 * q]) =
+          *reinterpret_cast<const vec16*>(ctx + (size_t)row * TD + 8 * q);
+    }
+  }
+  // lane (g, c16) of wave w holds, for row tile rt and column tile ct, rows
+  // r0 + 16rt + 4g + r (r < 4) of column 48w + 16ct + c16
+  float xv[TB_RT][TB_CT][4];
+#pragma unroll
+  for (int rt = 0; rt < TB_RT; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < TB_CT; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        xv[rt][ct][r] = a.x[(size_t)min(r0 + 16 * rt + 4 * g + r, a.M - 1) * TD + 48 * w + 16 * ct + c16];
+  __syncthreads();
+
+  f32x4 acc[TB_RT][TB_CT];
+  auto zero = [&]() {
+#pragma unroll
+    for (int rt = 0; rt < TB_RT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < TB_CT; ++ct) acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  // acc += (rows of src) x M^T over K = 192 for this wave's 3 column tiles t0 + ct
+  // (the product's 18 weight fragments are all requested before its first
+  // MFMA, so it waits for the L2 once instead of once per k-step)
+  auto product = [&](const bf16_t* src, const void* m, int K, int t0, int s0) {
+    bf16x8_t bw[TB_NK][TB_CT];
+#pragma unroll
+    for (int ks = 0; ks < TB_NK; ++ks)
+#pragma unroll
+      for (int ct = 0; ct < TB_CT; ++ct) bw[ks][ct] = frag(m, K, t0 + ct, s0 + ks);
+#pragma unroll
+    for (int ks = 0; ks < TB_NK; ++ks) {
+      bf16x8_t af[TB_RT];
+#pragma unroll
+      for (int rt = 0; rt < TB_RT; ++rt) af[rt] = M_::ld(&src[(16 * rt + c16) * TLH + ks * 32], lane);
+#pragma unroll
+      for (int rt = 0; rt < TB_RT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < TB_CT; ++ct) acc[rt][ct] = M_::mma(af[rt], bw[ks][ct], acc[rt][ct]);
+    }
+  };
+  // LayerNorm over the 192 columns of every row of v (in place), gamma/beta
+  // per column; the row sums are combined across the waves through LDS
+  auto layernorm = [&](float (&v)[TB_RT][TB_CT][4], const float* gm, const float* bt) {
+    float mean[TB_RT][4], rstd[TB_RT][4];
+#pragma unroll
+    for (int rt = 0; rt < TB_RT; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float s = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < TB_CT; ++ct) s += v[rt][ct][r];
+        s = row16_sum(s);
+        if (c16 == 0) red[w][16 * rt + 4 * g + r] = s;
+      }
+    __syncthreads();
+#pragma unroll
+    for (int rt = 0; rt < TB_RT; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * rt + 4 * g + r;
+        mean[rt][r] = ((red[0][row] + red[1][row]) + (red[2][row] + red[3][row])) * (1.0f / TD);
+      }
+    __syncthreads();
+#pragma unroll
+    for (int rt = 0; rt < TB_RT; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float q = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < TB_CT; ++ct) {
+          v[rt][ct][r] -= mean[rt][r];
+          q += v[rt][ct][r] * v[rt][ct][r];
+        }
+        q = row16_sum(q);
+        if (c16 == 0) red[w][16 * rt + 4 * g + r] = q;
+      }
+    __syncthreads();
+#pragma unroll
+    for (int rt = 0; rt < TB_RT; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * rt + 4 * g + r;
+        rstd[rt][r] = 1.0f / sqrtf(((red[0][row] + red[1][row]) + (red[2][row] + red[3][row])) *
+                                       (1.0f / TD) + 1e-5f);
+      }
+#pragma unroll
+    for (int ct = 0; ct < TB_CT; ++ct) {
+      const int col = 48 * w + 16 * ct + c16;
+      const float gg = gm[col], bb = bt[col];
+#pragma unroll
+      for (int rt = 0; rt < TB_RT; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[rt][ct][r] = v[rt][ct][r] * rstd[rt][r] * gg + bb;
+    }
+  };
+
+  // ---- x1 = LN1(x + ctx Wo^T + bo)
+  zero();
+  product(As, a.wo, TD, 3 * w, 0);
+#pragma unroll
+  for (int ct = 0; ct < TB_CT; ++ct) {
+    const float bo = a.bo[48 * w + 16 * ct + c16];
+#pragma unroll
+    for (int rt = 0; rt < TB_RT; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) xv[rt][ct][r] = xv[rt][ct][r] + (acc[rt][ct][r] + bo);
+  }
+  layernorm(xv, a.g1, a.be1);  // its barriers also end every wave's reads of ctx
+#pragma unroll
+  for (int rt = 0; rt < TB_RT; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < TB_CT; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        As[(16 * rt + 4 * g + r) * TLH + 48 * w + 16 * ct + c16] = f2bf(xv[rt][ct][r]);
+  __syncthreads();
+
+  // ---- y = relu(x1 W1^T + b1) W2^T over 4 hidden chunks of 192
+  f32x4 out[TB_RT][TB_CT];
+#pragma unroll
+  for (int rt = 0; rt < TB_RT; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < TB_CT; ++ct) out[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < TF / TD; ++c) {
+    zero();
+    product(As, a.w1, TD, c * (TD / 16) + 3 * w, 0);
+#pragma unroll
+    for (int ct = 0; ct < TB_CT; ++ct) {
+      const float b1 = a.b1[c * TD + 48 * w + 16 * ct + c16];
+#pragma unroll
+      for (int rt = 0; rt < TB_RT; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          Hs[(16 * rt + 4 * g + r) * TLH + 48 * w + 16 * ct + c16] =
+              f2bf(fmaxf(acc[rt][ct][r] + b1, 0.f));
+    }
+    bf16x8_t bw[TB_NK][TB_CT];  // requested before the barrier, in flight while it waits
+#pragma unroll
+    for (int ks = 0; ks < TB_NK; ++ks)
+#pragma unroll
+      for (int ct = 0; ct < TB_CT; ++ct) bw[ks][ct] = frag(a.w2, TF, 3 * w + ct, c * TB_NK + ks);
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < TB_NK; ++ks) {
+      bf16x8_t ah[TB_RT];
+#pragma unroll
+      for (int rt = 0; rt < TB_RT; ++rt) ah[rt] = M_::ld(&Hs[(16 * rt + c16) * TLH + ks * 32], lane);
+#pragma unroll
+      for (int rt = 0; rt < TB_RT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < TB_CT; ++ct) out[rt][ct] = M_::mma(ah[rt], bw[ks][ct], out[rt][ct]);
+    }
+    __syncthreads();  // the next chunk rewrites Hs
+  }
+
+  // ---- x <- LN2(x1 + y + b2), h <- bf16(x)
+#pragma unroll
+  for (int ct = 0; ct < TB_CT; ++ct) {
+    const float b2 = a.b2[48 * w + 16 * ct + c16];
+#pragma unroll
+    for (int rt = 0; rt < TB_RT; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) xv[rt][ct][r] = xv[rt][ct][r] + (out[rt][ct][r] + b2);
+  }
+  layernorm(xv, a.g2, a.be2);
+  bf16_t* h = static_cast<bf16_t*>(a.h);
+#pragma unroll
+  for (int rt = 0; rt < TB_RT; ++rt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = r0 + 16 * rt + 4 * g + r;
+      if (row >= a.M) continue;
+#pragma unroll
+      for (int ct = 0; ct < TB_CT; ++ct) {
+        const int col = 48 * w + 16 * ct + c16;
+        a.xo[(size_t)row * TD + col] = xv[rt][ct][r];
+        h[(size_t)row * TD + col] = f2bf(xv[rt][ct][r]);
+      }
+    }
+}
+
+void tf_layer_tp(const TfLayerArgs& a, hipStream_t s) {
+  if (a.M <= 0) return;
+  const double M = a.M;
+  klaunch(PROF_GEMM, 2.0 * M * TD * TD + 4.0 * M * TD * TF,
+          2.0 * M * TD + 4.0 * M * TD * 2 + 2.0 * (TD * TD + 2.0 * TD * TF) + 2.0 * M * TD,
+          tf_layer_tp_kernel, dim3((a.M + TB_RB - 1) / TB_RB), dim3(256), s, a);
+}
+
 int tf_tail(const TfTailArgs& a, hipStream_t s) {
   constexpr int NCH = SF_TFT_NCH, NW = SF_TFT_NW;
   if (a.M <= 0) return NCH;
