@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--no-profile", action="store_true", help="skip the profiled pass")
     ap.add_argument("--no-graphs", action="store_true",
                     help="launch the stream window forward kernel by kernel (no HIP graphs)")
+    ap.add_argument("--fixed-window", action="store_true",
+                    help="pad every stream window to the preset's capacity (one graph per stream)")
     ap.add_argument("--window-probe", type=int, default=0, metavar="W",
                     help="only run the encoder over one steady-state window of W frames of the "
                          "workload's model twice (a short program for counter collection) and exit")
@@ -362,6 +364,8 @@ def main():
     r = Runner(args.workload, wl, audio)
     if args.no_graphs and wl["mode"] == "stream":
         r.sf.sortformer_stream_set_option(r.stream.handle, r.sf.SF_STREAM_OPT_GRAPHS, 0)
+    if args.fixed_window and wl["mode"] == "stream":
+        r.sf.sortformer_stream_set_option(r.stream.handle, r.sf.SF_STREAM_OPT_FIXED_WINDOW, 1)
     for i in range(args.warmup):
         r.one_pass()
         torch.cuda.synchronize()

@@ -117,6 +117,23 @@ void sortformer_free(sf_model* model);
 /* The configuration the model was created with. SF_EINVAL on null pointers. */
 sf_status sortformer_get_config(const sf_model* model, sf_model_config* out);
 
+/* Model options.
+ * SF_OPT_OUTPUT_STRIDE (NEMOTRON): output frames of value x 10 ms, value in
+ *   {1, 2, 4, 8} (default 1, the head's 10 ms frames). The Transformers docs
+ *   "Nemotron 3 Diarization" (Overview) give the output frame resolution as
+ *   configurable in 10 ms steps with one checkpoint, and the model-card
+ *   summary in the ExecuTorch issue 10 ms as the default; the pages do not
+ *   say how a coarser frame is formed. Here output frame k is the mean of
+ *   the head's 10 ms probabilities value*k .. value*k + value - 1, and value
+ *   divides 8 so every 80 ms encoder frame holds a whole number of output
+ *   frames. Read by every later offline call and stream step of the model
+ *   (sortformer_stream_max_emit reflects it). SORTFORMER accepts only 1
+ *   (SF_EUNSUPPORTED otherwise); other values give SF_EINVAL. */
+#define SF_OPT_OUTPUT_STRIDE 1
+sf_status sortformer_set_option(sf_model* model, int32_t option, int32_t value);
+/* Current value of a model option (-1 for an unknown option or null model). */
+int32_t sortformer_get_option(const sf_model* model, int32_t option);
+
 /* Model metadata: the constants the "Streaming Sortformer Diarizer" model
  * card exports beside its methods (Exported Methods, Metadata:
  * sample_rate, window_stride, subsampling_factor, fc_d_model, tf_d_model,
@@ -171,7 +188,8 @@ size_t sortformer_offline_workspace_bytes(const sf_model* model, int32_t batch,
  *    n_out <= SF_MAX_WINDOW (the whole clip is one encoder window).
  *  NEMOTRON: the clip is processed in 30.4 s chunks with the arrival-order
  *    speaker cache and FIFO ("nemotron_offline" preset) and n_out =
- *    8*ceil(floor(N/160)/8) frames of 10 ms; any N.
+ *    (8/stride)*ceil(floor(N/160)/8) frames of stride x 10 ms
+ *    (SF_OPT_OUTPUT_STRIDE, default 1); any N.
  * *n_out_host receives n_out before any work is enqueued. */
 sf_status sortformer_forward_offline(sf_model* model, const float* d_audio, int32_t batch,
                                      int64_t n_samples, float* d_probs, int64_t* n_out_host,
@@ -218,7 +236,8 @@ sf_status sortformer_stream_reset(sf_stream* st, void* stream);
  * step 0 needs 1280*(chunk+right_context)+40, later steps 1280*chunk. */
 int64_t sortformer_stream_samples_needed(const sf_stream* st);
 /* Upper bound of frames any step emits per stream (for sizing d_probs_out):
- * chunk_len for SORTFORMER, 8*chunk_len for NEMOTRON. */
+ * chunk_len + right_context for SORTFORMER, (8/stride) times that for
+ * NEMOTRON (SF_OPT_OUTPUT_STRIDE of the model at the time of the call). */
 int32_t sortformer_stream_max_emit(const sf_stream* st);
 
 /* One streaming step (NeMo forward_streaming_step; Transformers model call
@@ -341,6 +360,18 @@ sf_status sortformer_stream_set_rows(sf_stream* st, int32_t cache_len, int32_t f
  * off, first waits for the device once and releases the old graphs; steps
  * with an unchanged workspace never synchronise the host. */
 #define SF_STREAM_OPT_GRAPHS 1
+/* SF_STREAM_OPT_FIXED_WINDOW (default 0): with 1 every step's window forward
+ * runs at one fixed size, the stream's capacity (spkcache_len + fifo_len +
+ * chunk_len + right_context rows), with the rows past the current window
+ * zeroed and masked: the valid length is written to the workspace by a small
+ * kernel before each window forward and every kernel that masks reads it
+ * there. One graph per ping-pong buffer then serves every step (the
+ * Transformers docs "Nemotron 3 Diarization", fixed-window section: pad to
+ * max_window so that one compiled graph serves the whole stream), at the cost
+ * of computing the padded rows. Valid rows are unchanged by the padding
+ * (bit for bit while the padded and unpadded windows fall on the same side
+ * of the 4096-row kernel regimes). */
+#define SF_STREAM_OPT_FIXED_WINDOW 2
 sf_status sortformer_stream_set_option(sf_stream* st, int32_t option, int32_t value);
 
 /* Test hook — the cache update alone ("Streaming Sortformer Diarizer" model

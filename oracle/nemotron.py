@@ -14,6 +14,13 @@ exact (erf) GELU, FFN 2048, 8 heads of 64, scale 1/8; RoPE rotate-half with
 base 10000 and positions 0..W-1 of the window; final LN; head Linear 512->8
 (80 ms logits) then ConvTranspose1d(8, 8, kernel 8, stride 8) to 10 ms and
 a sigmoid. The speaker cache is scored with sigmoid of the 80 ms logits.
+
+Output resolution (Transformers docs "Nemotron 3 Diarization", Overview: one
+checkpoint, output frame resolution configurable in 10 ms steps; the
+model-card summary: 10 ms by default). Reading: a resolution of r x 10 ms
+with r in {1, 2, 4, 8} (so an 80 ms encoder frame holds a whole number of
+output frames) gives output frame k the mean of the head's 10 ms
+probabilities r k .. r k + r - 1.
 """
 from __future__ import annotations
 
@@ -82,6 +89,19 @@ def upsample_head(w, logits80):
     W, S = logits80.shape
     up = np.einsum("ti,ior->tro", logits80, w["up.w"]) + w["up.b"]
     return up.reshape(8 * W, S)
+
+
+OUTPUT_STRIDES = (1, 2, 4, 8)
+
+
+def pool_output(probs10, r):
+    """(8W, S) probabilities at 10 ms -> (8W / r, S) at r x 10 ms: the mean of
+    each run of r consecutive frames."""
+    if r not in OUTPUT_STRIDES:
+        raise ValueError(f"output stride {r} not in {OUTPUT_STRIDES}")
+    n, S = probs10.shape
+    assert n % r == 0
+    return probs10.reshape(n // r, r, S).mean(axis=1)
 
 
 def encode_window(w, emb, n_valid=None, n_layers=N_LAYERS):

@@ -146,9 +146,23 @@ void drop_graphs(sf_stream* st) {
   st->graphs.clear();
 }
 
-// Window copy + encoder for the current state, enqueued on s.
+// Rows per stream of the window forward: the window itself, or the whole
+// capacity when windows are padded to one fixed size.
+int window_rows(const sf_stream* st) {
+  return st->fixed_window ? st->cap : st->Lc + st->Lf + st->Lp;
+}
+
+// Window copy + encoder for the current state, enqueued on s. A fixed window
+// copies all cap rows, zeroing those at or past the valid length that the
+// kernels read from enc.nv (set by the caller of this function).
 void window_forward(sf_stream* st, EncWs& enc, hipStream_t s) {
   const int W = st->Lc + st->Lf + st->Lp;
+  if (st->fixed_window) {
+    copy_rows_nv(st->E[st->cur], (long long)st->cap * st->D, st->D, enc.x,
+                 (long long)st->cap * st->D, st->D, st->B, st->cap, st->D, enc.nv, s);
+    encode(st->m, enc, st->B, st->cap, st->cap, s, false, enc.nv);
+    return;
+  }
   copy_rows(st->E[st->cur], (long long)st->cap * st->D, st->D, enc.x, (long long)W * st->D, st->D,
             st->B, W, st->D, s);
   encode(st->m, enc, st->B, W, W, s);
@@ -157,7 +171,7 @@ void window_forward(sf_stream* st, EncWs& enc, hipStream_t s) {
 // Runs window_forward, through a cached graph when enabled. Returns false if
 // capture or instantiation failed (then the direct launch path was used).
 bool window_forward_graph(sf_stream* st, EncWs& enc, const void* ws, hipStream_t s) {
-  const int W = st->Lc + st->Lf + st->Lp;
+  const int W = window_rows(st);
   if (ws != st->graph_ws) {  // graphs of one workspace at a time: at most 2 per window size
     drop_graphs(st);
     st->graph_ws = ws;
@@ -188,7 +202,9 @@ bool window_forward_graph(sf_stream* st, EncWs& enc, const void* ws, hipStream_t
 void step_core(sf_stream* st, int n_chunk, float* out, long long out_bstride, EncWs& enc,
                const void* ws, hipStream_t s) {
   const sf_model* m = st->m;
-  const int W = st->Lc + st->Lf + st->Lp, S = st->S, B = st->B;
+  const int S = st->S, B = st->B;
+  const int W = window_rows(st);  // row pitch of the window's outputs
+  if (st->fixed_window) fill_i32(enc.nv, 1, st->Lc + st->Lf + st->Lp, s);
   bool done = false;
   if (st->use_graphs && ws && !profiling()) done = window_forward_graph(st, enc, ws, s);
   if (!done) {
@@ -198,9 +214,12 @@ void step_core(sf_stream* st, int n_chunk, float* out, long long out_bstride, En
   const int r0 = st->Lc + st->Lf;
   if (m->cfg.arch == SF_ARCH_SORTFORMER)
     copy_rows(enc.probs + (size_t)r0 * S, (long long)W * S, S, out, out_bstride, S, B, n_chunk, S, s);
-  else
+  else if (m->out_stride == 1)
     copy_rows(enc.probs10 + (size_t)8 * r0 * S, (long long)8 * W * S, S, out, out_bstride, S, B,
               8 * n_chunk, S, s);
+  else
+    pool_rows(enc.probs10 + (size_t)8 * r0 * S, (long long)8 * W * S, out, out_bstride, B,
+              8 * n_chunk / m->out_stride, m->out_stride, S, s);
   state_update(st, enc.probs, W, n_chunk, s);
 }
 
@@ -259,6 +278,7 @@ sf_status sortformer_init(const sf_model_config* cfg, uint64_t seed, void* d_wei
   if (!m) return SF_ENOMEM;
   m->cfg = *cfg;
   m->seed = seed;
+  m->out_stride = 1;
   const sf_status st = init_model(m, d_weights, bytes, HS(stream));
   if (st != SF_OK) {
     delete m;
@@ -383,7 +403,8 @@ sf_status sortformer_forward_offline(sf_model* m, const float* d_audio, int32_t 
     return launched();
   }
   // Nemotron-style: 30.4 s chunks with the arrival-order cache and FIFO.
-  *n_out = 8LL * Te;
+  const int per = 8 / m->out_stride;  // output frames per encoder frame
+  *n_out = (long long)per * Te;
   if (Te == 0) return SF_OK;
   sf_stream st{};
   st.m = m;
@@ -413,7 +434,8 @@ sf_status sortformer_forward_offline(sf_model* m, const float* d_audio, int32_t 
               e1 - st.enc_done, 512, s);
     st.Lp += e1 - st.enc_done;
     st.enc_done = e1;
-    step_core(&st, c1 - c0, d_probs + (size_t)8 * c0 * S, (long long)8 * Te * S, enc, nullptr, s);
+    step_core(&st, c1 - c0, d_probs + (size_t)per * c0 * S, (long long)per * Te * S, enc, nullptr,
+              s);
   }
   return launched();
 }
@@ -445,6 +467,7 @@ sf_status sortformer_stream_create(sf_model* m, const sf_stream_config* c, int32
   st->cap = stream_cap(c);
   st->ring_cap = ring_cap_for(c);
   st->use_graphs = true;
+  st->fixed_window = false;
   st->cap_stream = nullptr;
   st->graph_ws = nullptr;
   bind_state(st, static_cast<char*>(d_state));
@@ -472,6 +495,11 @@ sf_status sortformer_stream_set_option(sf_stream* st, int32_t option, int32_t va
     if (!st->use_graphs) drop_graphs(st);
     return SF_OK;
   }
+  if (option == SF_STREAM_OPT_FIXED_WINDOW) {
+    if ((value != 0) != st->fixed_window) drop_graphs(st);  // keys change meaning
+    st->fixed_window = value != 0;
+    return SF_OK;
+  }
   return SF_EINVAL;
 }
 
@@ -492,7 +520,23 @@ int64_t sortformer_stream_samples_needed(const sf_stream* st) {
 int32_t sortformer_stream_max_emit(const sf_stream* st) {
   if (!st) return 0;
   const int n = st->sc.chunk_len + st->sc.right_context;
-  return st->m->cfg.arch == SF_ARCH_NEMOTRON ? 8 * n : n;
+  return st->m->cfg.arch == SF_ARCH_NEMOTRON ? 8 / st->m->out_stride * n : n;
+}
+
+sf_status sortformer_set_option(sf_model* m, int32_t option, int32_t value) {
+  if (!m) return SF_EINVAL;
+  if (option == SF_OPT_OUTPUT_STRIDE) {
+    if (value != 1 && value != 2 && value != 4 && value != 8) return SF_EINVAL;
+    if (m->cfg.arch != SF_ARCH_NEMOTRON && value != 1) return SF_EUNSUPPORTED;
+    m->out_stride = value;
+    return SF_OK;
+  }
+  return SF_EINVAL;
+}
+
+int32_t sortformer_get_option(const sf_model* m, int32_t option) {
+  if (!m) return -1;
+  return option == SF_OPT_OUTPUT_STRIDE ? m->out_stride : -1;
 }
 
 }  // extern "C"
@@ -545,7 +589,9 @@ void step_from_ring(sf_stream* st, const StepPlan& p, bool is_last, float* out,
   st->finished = is_last;
 }
 
-int emit_rate(const sf_stream* st) { return st->m->cfg.arch == SF_ARCH_NEMOTRON ? 8 : 1; }
+int emit_rate(const sf_stream* st) {
+  return st->m->cfg.arch == SF_ARCH_NEMOTRON ? 8 / st->m->out_stride : 1;
+}
 
 // The steps a feed of n_new more samples runs, on a copy of the counters: the
 // non-final steps whose audio is complete, then (is_last) the final step.

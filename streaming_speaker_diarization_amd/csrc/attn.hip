@@ -195,7 +195,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) { mrow[r] = -INFINITY; lrow[r] = 0.f; }
 
-  const int ntile = (a.n_valid + 63) / 64;
+  const int n_valid = a.nv ? *a.nv : a.n_valid;
+  const int ntile = (n_valid + 63) / 64;
   if (w < ntile) load_kb(w * 64);
   for (int kt = w; kt < ntile; kt += NW) {
     const int j0 = kt * 64;
@@ -277,12 +278,12 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     // ---- online softmax (log2 domain: the running max is kept scaled by
     // scale*log2(e), p = 2^(s*scale*log2(e) - m)); keys past n_valid exist
     // only in the last tile
-    if (j0 + 64 > a.n_valid) {
+    if (j0 + 64 > n_valid) {
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          S[nt][r] = j0 + 16 * nt + c16 < a.n_valid ? S[nt][r] : -INFINITY;
+          S[nt][r] = j0 + 16 * nt + c16 < n_valid ? S[nt][r] : -INFINITY;
     }
     float mx[4];
 #pragma unroll
@@ -568,7 +569,8 @@ void attn_tp_kernel(AttnArgs a) {
     for (int dt = 0; dt < NDT; ++dt) O[s][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};  // lrow: this lane's keys
 
-  const int ntile = (a.n_valid + 63) / 64;
+  const int n_valid = a.nv ? *a.nv : a.n_valid;
+  const int ntile = (n_valid + 63) / 64;
   fetch(0);
   for (int kt = 0; kt < ntile; ++kt) {
     const int j0 = kt * 64;
@@ -628,14 +630,14 @@ void attn_tp_kernel(AttnArgs a) {
     // ---- online softmax (log2 domain: the running max is kept scaled by
     // scale*log2(e), p = 2^(s*scale*log2(e) - m)); P^T as the B operand of
     // O^T += V^T P^T. Keys past n_valid exist only in the last tile.
-    if (j0 + 64 > a.n_valid) {
+    if (j0 + 64 > n_valid) {
 #pragma unroll
       for (int s = 0; s < 2; ++s)
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            S[s][nt][r] = j0 + 16 * nt + 4 * g + r < a.n_valid ? S[s][nt][r] : -INFINITY;
+            S[s][nt][r] = j0 + 16 * nt + 4 * g + r < n_valid ? S[s][nt][r] : -INFINITY;
     }
     bf16x8_t pb[2][2];
 #pragma unroll

@@ -594,6 +594,7 @@ __global__ __launch_bounds__(256) void gemm_slice_dma_kernel(GemmArgs g) {
 #pragma unroll
     for (int t = 0; t < 9; ++t) w9[t] = g.dw_w9[ch * 9 + t];
     const float sc = g.dw_sc[ch], sh = g.dw_sh[ch];
+    const int nvv = g.dw_nv ? *g.dw_nv : g.dw_nvalid;
     int fr = (m0 + r0) % g.dw_W;
     bf16_t* out = static_cast<bf16_t*>(g.out);
 #pragma unroll
@@ -603,7 +604,7 @@ __global__ __launch_bounds__(256) void gemm_slice_dma_kernel(GemmArgs g) {
 #pragma unroll
       for (int t = 0; t < 9; ++t) {
         const int tt = fr + t - 4;
-        acc += (tt >= 0 && tt < g.dw_nvalid) ? w9[t] * cs[(r + t) * LDC + c] : 0.f;
+        acc += (tt >= 0 && tt < nvv) ? w9[t] * cs[(r + t) * LDC + c] : 0.f;
       }
       if (m < g.M) out[(size_t)m * g.ldo + ch] = f2bf(swishf_(sc * acc + sh));
       fr = fr + 1 == g.dw_W ? 0 : fr + 1;

@@ -75,6 +75,8 @@ struct sf_model {
   const float *fin_g, *fin_b, *nh_w, *nh_b, *up_w, *up_b, *rope;
   // frontend tables
   const float* fe_tab;
+  // NEMOTRON output frames: 10 ms x out_stride (1, 2, 4 or 8)
+  int out_stride;
   // per-layer taps honoured by sortformer_encode_window
   std::vector<Tap> taps;
 };
@@ -103,6 +105,7 @@ struct sf_stream {
   // window-forward graphs keyed by (window rows, ping-pong buffer, workspace)
   // (HIP handles kept opaque here: this header is also built by the host compiler)
   bool use_graphs;
+  bool fixed_window;  // every window padded to cap rows, one graph per ping-pong buffer
   void* cap_stream;                                            // hipStream_t
   std::map<std::tuple<int, int, const void*>, void*> graphs;   // hipGraphExec_t
   const void* graph_ws;  // the workspace the cached graphs were captured with

@@ -36,6 +36,7 @@ struct GemmArgs {
   // frame; frames at or past dw_nvalid count as zero).
   const float* dw_w9; const float* dw_sc; const float* dw_sh;
   int dw_W, dw_nvalid;
+  const int* dw_nv;  // when non-null: device copy of the valid frame count, read instead
 };
 // EPI_PARTIAL writes fp32 partial sums (no bias) to out as [slice][M][N] and
 // returns the slice count; other epilogues return 1.
@@ -59,6 +60,7 @@ struct AttnArgs {
   int qoff, koff;
   const void* vt; int vpitch; // V transposed per head: (B, H, hd, vpitch), keys contiguous
   int B, H, W, n_valid;
+  const int* nv;      // when non-null: device copy of n_valid, read instead (fixed windows)
   const float* ub; const float* vb;   // (H, hd) relative-position biases
   const void* P; int ldp; int p_center; // relative-position projections, row delta+p_center
   const float* rope;                  // (max_window, hd/2) (cos, sin) pairs
@@ -116,7 +118,8 @@ struct TfLayerArgs {
 };
 void tf_layer_tp(const TfLayerArgs& a, hipStream_t s);
 
-void dwconv_time(const float* glu, int B, int W, int n_valid, const float* w9,
+// nv (may be null): device copy of n_valid, read instead when given
+void dwconv_time(const float* glu, int B, int W, int n_valid, const int* nv, const float* w9,
                  const float* scale, const float* shift, void* out, bool bf16, hipStream_t s);
 
 void logmel(const float* audio, long long a_bstride, long long ring_mask, long long n_total,
@@ -139,6 +142,14 @@ void head_nemotron(const float* x, int M, const float* hw, const float* hb, cons
 
 void copy_rows(const float* src, long long s_bstride, int s_ld, float* dst, long long d_bstride,
                int d_ld, int B, int rows, int cols, hipStream_t s);
+// dst[b][k][c] = mean of src[b][r k + q][c] over q < r (rows of S = cols
+// floats, dense): n_out output rows per batch
+void pool_rows(const float* src, long long s_bstride, float* dst, long long d_bstride, int B,
+               int n_out, int r, int cols, hipStream_t s);
+// copy_rows for `rows` rows per batch where rows at or past the device count
+// *nv are written as zeros
+void copy_rows_nv(const float* src, long long s_bstride, int s_ld, float* dst, long long d_bstride,
+                  int d_ld, int B, int rows, int cols, const int* nv, hipStream_t s);
 // n contiguous elements (fp32, or bf16 when src_bf16) widened to fp32
 void widen(const void* src, bool src_bf16, float* dst, long long n, hipStream_t s);
 // n samples of each stream (stream b's at src + b*src_bstride) into the audio

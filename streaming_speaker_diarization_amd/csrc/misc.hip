@@ -151,9 +151,10 @@ void layernorm(const LnArgs& a, bool bf16, hipStream_t s) {
 // of them in registers (16-byte loads, each input row loaded once).
 #define DW_ROWS 4
 template <typename T>
-__global__ __launch_bounds__(128) void dwconv_time_kernel(const float* glu, int W, int n_valid,
-                                                          const float* w9, const float* sc,
-                                                          const float* sh, T* out) {
+__global__ __launch_bounds__(128) void dwconv_time_kernel(const float* glu, int W, int n_valid_h,
+                                                          const int* nv, const float* w9,
+                                                          const float* sc, const float* sh, T* out) {
+  const int n_valid = nv ? *nv : n_valid_h;
   // XCD-aware order (bijection over the grid): physical workgroup i runs on
   // XCD i % 8, and XCD x takes a contiguous range of (stream, row block), so
   // the halo rows that neighbouring blocks share come from one L2
@@ -214,17 +215,17 @@ __global__ __launch_bounds__(128) void dwconv_time_kernel(const float* glu, int 
   }
 }
 
-void dwconv_time(const float* glu, int B, int W, int n_valid, const float* w9, const float* sc,
-                 const float* sh, void* out, bool bf16, hipStream_t s) {
+void dwconv_time(const float* glu, int B, int W, int n_valid, const int* nv, const float* w9,
+                 const float* sc, const float* sh, void* out, bool bf16, hipStream_t s) {
   if (W <= 0) return;
   const double fl = 2.0 * 9 * 512 * B * W, by = (double)B * W * 512 * (4.0 + (bf16 ? 2 : 4));
   dim3 grid((W + DW_ROWS - 1) / DW_ROWS, B);
   if (bf16)
-    klaunch(PROF_CONV, fl, by, dwconv_time_kernel<bf16_t>, grid, dim3(128), s, glu, W, n_valid, w9,
-            sc, sh, static_cast<bf16_t*>(out));
+    klaunch(PROF_CONV, fl, by, dwconv_time_kernel<bf16_t>, grid, dim3(128), s, glu, W, n_valid, nv,
+            w9, sc, sh, static_cast<bf16_t*>(out));
   else
-    klaunch(PROF_CONV, fl, by, dwconv_time_kernel<float>, grid, dim3(128), s, glu, W, n_valid, w9,
-            sc, sh, static_cast<float*>(out));
+    klaunch(PROF_CONV, fl, by, dwconv_time_kernel<float>, grid, dim3(128), s, glu, W, n_valid, nv,
+            w9, sc, sh, static_cast<float*>(out));
 }
 
 // ------------------------------------------------------------ log-mel
@@ -605,6 +606,22 @@ void copy_rows(const float* src, long long sb, int sl, float* dst, long long db,
                      sl, dst, db, dl, cols);
 }
 
+__global__ void copy_rows_nv_kernel(const float* src, long long sb, int sl, float* dst,
+                                    long long db, int dl, int cols, const int* nv) {
+  const int r = blockIdx.x, b = blockIdx.y;
+  const bool live = r < *nv;
+  const float* sp = src + (size_t)b * sb + (size_t)r * sl;
+  float* dp = dst + (size_t)b * db + (size_t)r * dl;
+  for (int c = threadIdx.x; c < cols; c += blockDim.x) dp[c] = live ? sp[c] : 0.f;
+}
+
+void copy_rows_nv(const float* src, long long sb, int sl, float* dst, long long db, int dl, int B,
+                  int rows, int cols, const int* nv, hipStream_t s) {
+  if (rows <= 0 || B <= 0) return;
+  hipLaunchKernelGGL(copy_rows_nv_kernel, dim3(rows, B), dim3(cols >= 256 ? 256 : 64), 0, s, src,
+                     sb, sl, dst, db, dl, cols, nv);
+}
+
 __global__ void widen_kernel(const void* src, bool bf, float* dst, long long n) {
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
   if (i < n)
@@ -615,6 +632,24 @@ void widen(const void* src, bool src_bf16, float* dst, long long n, hipStream_t 
   if (n <= 0) return;
   hipLaunchKernelGGL(widen_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src,
                      src_bf16, dst, n);
+}
+
+__global__ void pool_rows_kernel(const float* src, long long s_bstride, float* dst,
+                                 long long d_bstride, int n_out, int r, int cols) {
+  const int i = blockIdx.x * 256 + threadIdx.x, b = blockIdx.y;
+  if (i >= n_out * cols) return;
+  const int k = i / cols, c = i % cols;
+  const float* p = src + (size_t)b * s_bstride + (size_t)k * r * cols + c;
+  float acc = 0.f;
+  for (int q = 0; q < r; ++q) acc += p[(size_t)q * cols];
+  dst[(size_t)b * d_bstride + (size_t)k * cols + c] = acc / (float)r;
+}
+
+void pool_rows(const float* src, long long s_bstride, float* dst, long long d_bstride, int B,
+               int n_out, int r, int cols, hipStream_t s) {
+  if (n_out <= 0 || B <= 0) return;
+  hipLaunchKernelGGL(pool_rows_kernel, dim3((n_out * cols + 255) / 256, B), dim3(256), 0, s, src,
+                     s_bstride, dst, d_bstride, n_out, r, cols);
 }
 
 __global__ void ring_write_kernel(const float* src, long long src_bstride, long long n,

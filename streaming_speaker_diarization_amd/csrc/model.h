@@ -18,6 +18,7 @@ struct EncWs {
   size_t part_floats;
   void* vt;       // (B, H, head dim, vpitch) V transposed per head
   int vpitch;     // keys per V^T row (window rounded up to 8)
+  int* nv;        // one int: the valid window length of a fixed padded window
 };
 
 bool valid_config(const sf_model_config* c);
@@ -30,8 +31,10 @@ void pre_encode_range(const sf_model* m, const float* audio, long long a_bstride
                       long long ring_mask, long long n_total, int T, int e0, int e1, int B,
                       float* dst, long long dst_bstride, char* wsp, hipStream_t s);
 // taps: honour m->taps (the caller has checked their capacities)
+// nv (may be null): device copy of n_valid, which the kernels then read instead
+// (windows of a fixed padded size whose valid length changes per replay)
 void encode(const sf_model* m, EncWs& w, int B, int W, int n_valid, hipStream_t s,
-            bool taps = false);
+            bool taps = false, const int* nv = nullptr);
 int tap_layers(const sf_model* m);
 int tap_width(const sf_model* m, int layer);
 

@@ -445,6 +445,7 @@ size_t enc_ws_bytes(const sf_model* m, int B, int W) {
   t += al(r * 64 * 4);    // probs10
   t += al(part_floats(r) * 4);
   t += al((size_t)B * 512 * (W + 8) * es);  // V transposed per head
+  t += 256;                                  // valid length of a fixed window
   return t;
 }
 
@@ -467,6 +468,7 @@ EncWs carve_enc(const sf_model* m, char* p, int B, int W) {
   w.part = reinterpret_cast<float*>(take(w.part_floats * 4));
   w.vpitch = (W + 7) / 8 * 8;
   w.vt = take((size_t)B * 512 * (W + 8) * es);
+  w.nv = reinterpret_cast<int*>(take(256));
   return w;
 }
 
@@ -622,7 +624,7 @@ int tap_width(const sf_model* m, int layer) {
 }
 
 static void encode_sortformer(const sf_model* m, EncWs& w, int B, int W, int n_valid,
-                              hipStream_t s, const Taps& tp) {
+                              hipStream_t s, const Taps& tp, const int* nv) {
   const bool bf = m->bf16;
   Ctx c{m, w, B * W, s, bf};
   c.ln(512, 0, nullptr, 0.f, m->conf[0].ff1_g, m->conf[0].ff1_b, nullptr, nullptr, 0, w.h);
@@ -637,7 +639,7 @@ static void encode_sortformer(const sf_model* m, EncWs& w, int B, int W, int n_v
     c.qkv(w.h, 512, L.wqkv, L.bqkv, w.big, 64, W);
     AttnArgs a{};
     a.qkv = w.big; a.ldq = 1536; a.qoff = 0; a.koff = 512; a.vt = w.vt; a.vpitch = w.vpitch;
-    a.B = B; a.H = 8; a.W = W; a.n_valid = n_valid;
+    a.B = B; a.H = 8; a.W = W; a.n_valid = n_valid; a.nv = nv;
     a.ub = L.u; a.vb = L.v; a.P = L.P; a.ldp = 512; a.p_center = SF_MAX_WINDOW - 1;
     a.ctx = w.ctx; a.ldc = 512; a.scale = 0.125f;
     // windows in the latency form: the output projection's per-head partial
@@ -656,11 +658,12 @@ static void encode_sortformer(const sf_model* m, EncWs& w, int B, int W, int n_v
       g.A = w.h; g.lda = 512; g.W = L.pw1; g.ldw = 512; g.bias = L.pw1_b;
       g.M = B * W; g.N = 1024; g.K = 512; g.out = w.ctx; g.ldo = 512;
       g.dw_w9 = L.dw9; g.dw_sc = L.dw_sc; g.dw_sh = L.dw_sh; g.dw_W = W; g.dw_nvalid = n_valid;
+      g.dw_nv = nv;
       gemm_glu_dwconv(g, s);
       ns = c.branch(w.ctx, 512, L.pw2, 512, 512);
     } else {
       c.lin(w.h, 512, L.pw1, L.pw1_b, 1024, 512, w.glu, 512, EPI_GLU, false);
-      dwconv_time(w.glu, B, W, n_valid, L.dw9, L.dw_sc, L.dw_sh, w.h, bf, s);
+      dwconv_time(w.glu, B, W, n_valid, nv, L.dw9, L.dw_sc, L.dw_sh, w.h, bf, s);
       ns = c.branch(w.h, 512, L.pw2, 512, 512);
     }
     c.ln(512, ns, L.pw2_b, 1.f, L.ff2_g, L.ff2_b, nullptr, nullptr, 1, w.h);
@@ -686,7 +689,7 @@ static void encode_sortformer(const sf_model* m, EncWs& w, int B, int W, int n_v
     c.qkv(hin, 192, L.wqkv, L.bqkv, w.big, 24, W);
     AttnArgs a{};
     a.qkv = w.big; a.ldq = 576; a.qoff = 0; a.koff = 192; a.vt = w.vt; a.vpitch = w.vpitch;
-    a.B = B; a.H = 8; a.W = W; a.n_valid = n_valid;
+    a.B = B; a.H = 8; a.W = W; a.n_valid = n_valid; a.nv = nv;
     a.ctx = w.ctx; a.ldc = 192; a.scale = 1.0f / std::sqrt(24.0f);
     attention(a, ATT_PLAIN, 24, bf, s);
     tp.at(17 + l, SF_TAP_ATTN_CTX, w.ctx, bf, 192);
@@ -724,7 +727,7 @@ static void encode_sortformer(const sf_model* m, EncWs& w, int B, int W, int n_v
 }
 
 static void encode_nemotron(const sf_model* m, EncWs& w, int B, int W, int n_valid,
-                            hipStream_t s, const Taps& tp) {
+                            hipStream_t s, const Taps& tp, const int* nv) {
   const bool bf = m->bf16;
   Ctx c{m, w, B * W, s, bf};
   c.ln(512, 0, nullptr, 0.f, m->rl[0].ln1_g, m->rl[0].ln1_b, nullptr, nullptr, 0, w.h);
@@ -734,7 +737,7 @@ static void encode_nemotron(const sf_model* m, EncWs& w, int B, int W, int n_val
     c.qkv(w.h, 512, L.wqkv, L.bqkv, w.big, 64, W);
     AttnArgs a{};
     a.qkv = w.big; a.ldq = 1536; a.qoff = 0; a.koff = 512; a.vt = w.vt; a.vpitch = w.vpitch;
-    a.B = B; a.H = 8; a.W = W; a.n_valid = n_valid; a.rope = m->rope;
+    a.B = B; a.H = 8; a.W = W; a.n_valid = n_valid; a.nv = nv; a.rope = m->rope;
     a.ctx = w.ctx; a.ldc = 512; a.scale = 0.125f;
     const bool fuse_wo = bf && B * W <= SLICE_MAX_ROWS;  // as in the conformer layers
     if (fuse_wo) { a.wo_f = L.wo_f; a.part = w.part; a.M = B * W; }
@@ -753,10 +756,11 @@ static void encode_nemotron(const sf_model* m, EncWs& w, int B, int W, int n_val
   head_nemotron(w.x, B * W, m->nh_w, m->nh_b, m->up_w, m->up_b, w.probs, w.probs10, s);
 }
 
-void encode(const sf_model* m, EncWs& w, int B, int W, int n_valid, hipStream_t s, bool taps) {
+void encode(const sf_model* m, EncWs& w, int B, int W, int n_valid, hipStream_t s, bool taps,
+            const int* nv) {
   const Taps tp{m, taps && !m->taps.empty(), (long long)B * W, s};
-  if (m->cfg.arch == SF_ARCH_SORTFORMER) encode_sortformer(m, w, B, W, n_valid, s, tp);
-  else encode_nemotron(m, w, B, W, n_valid, s, tp);
+  if (m->cfg.arch == SF_ARCH_SORTFORMER) encode_sortformer(m, w, B, W, n_valid, s, tp, nv);
+  else encode_nemotron(m, w, B, W, n_valid, s, tp, nv);
 }
 
 }  // namespace sfm

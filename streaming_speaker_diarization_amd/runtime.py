@@ -36,6 +36,13 @@ class Model:
             sf.sortformer_free(h)
             self.handle = None
 
+    def set_output_stride(self, r: int):
+        """Nemotron: output frames of r x 10 ms (r in 1, 2, 4, 8)."""
+        sf.sortformer_set_option(self.handle, sf.SF_OPT_OUTPUT_STRIDE, r)
+
+    def output_stride(self) -> int:
+        return sf.sortformer_get_option(self.handle, sf.SF_OPT_OUTPUT_STRIDE)
+
     def metadata(self) -> dict:
         return sf.sortformer_get_metadata(self.handle)
 
@@ -48,7 +55,7 @@ class Model:
         B, N = audio.shape
         ws = self.workspace(sf.sortformer_offline_workspace_bytes(self.handle, B, N))
         te = (N // 160 + 7) // 8
-        n_out = te if self.arch == "sortformer" else 8 * te
+        n_out = te if self.arch == "sortformer" else 8 // self.output_stride() * te
         out = torch.empty(B, max(n_out, 1), self.n_spk, dtype=torch.float32, device=self.device)
         got = sf.sortformer_forward_offline(self.handle, audio.contiguous(), out, ws)
         return out[:, :got]

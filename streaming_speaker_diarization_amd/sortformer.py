@@ -29,7 +29,7 @@ EXPORTS = [
     "sortformer_stream_get_info", "sortformer_stream_export", "sortformer_stream_import",
     "sortformer_stream_checkpoint_bytes", "sortformer_stream_get_rows", "sortformer_stream_set_rows",
     "sortformer_stream_feed", "sortformer_stream_feed_frames", "sortformer_get_metadata",
-    "sortformer_stream_step_noalloc",
+    "sortformer_stream_step_noalloc", "sortformer_set_option", "sortformer_get_option",
     "sortformer_stream_update",
     "sortformer_encode_workspace_bytes", "sortformer_encode_window", "sortformer_pre_encode",
     "sortformer_pre_encode_workspace_bytes", "sortformer_config_num_tensors",
@@ -38,6 +38,8 @@ EXPORTS = [
     "sortformer_segments", "sortformer_debug_tap",
 ]
 SF_STREAM_OPT_GRAPHS = 1
+SF_STREAM_OPT_FIXED_WINDOW = 2
+SF_OPT_OUTPUT_STRIDE = 1
 SF_NOALLOC_SCRATCH_BYTES = 64 << 20
 SF_TAP_LAYER_IN, SF_TAP_ATTN_CTX, SF_TAP_LAYER_OUT = 0, 1, 2
 SF_MAX_TAPS = 16
@@ -128,6 +130,8 @@ def load(path: str = LIB_PATH):
         "sortformer_stream_feed": (I32, [P, P, I64, I32, P, I64, C.POINTER(I64), P, SZ, P]),
         "sortformer_stream_feed_frames": (I64, [P, I64, I32]),
         "sortformer_stream_step_noalloc": (I32, [P, P, I64, I32, P, C.POINTER(I32), P]),
+        "sortformer_set_option": (I32, [P, I32, I32]),
+        "sortformer_get_option": (I32, [P, I32]),
         "sortformer_get_metadata": (I32, [P, C.POINTER(sf_model_metadata)]),
         "sortformer_stream_update": (I32, [P, P, I32, P, SZ, P]),
         "sortformer_encode_workspace_bytes": (SZ, [P, I32, I32]),
@@ -227,6 +231,14 @@ def sortformer_free(h):
     load().sortformer_free(h)
 
 
+def sortformer_set_option(h, option, value):
+    _check(load().sortformer_set_option(h, option, int(value)), "set_option")
+
+
+def sortformer_get_option(h, option) -> int:
+    return load().sortformer_get_option(h, option)
+
+
 def sortformer_get_metadata(h) -> dict:
     md = sf_model_metadata()
     _check(load().sortformer_get_metadata(h, C.byref(md)), "get_metadata")
@@ -281,7 +293,8 @@ def sortformer_forward_offline(h, d_audio, d_probs, d_ws, stream=None) -> int:
     cfg = sf_model_config()
     _check(load().sortformer_get_config(h, C.byref(cfg)), "get_config")
     te = (N // 160 + 7) // 8
-    rows = te if cfg.arch == SF_ARCH_SORTFORMER else 8 * te
+    rows = te if cfg.arch == SF_ARCH_SORTFORMER else \
+        8 // sortformer_get_option(h, SF_OPT_OUTPUT_STRIDE) * te
     _check(load().sortformer_forward_offline(h, _ptr(d_audio), B, N,
                                              _ptr(d_probs, B * rows * cfg.n_spk),
                                              C.byref(n_out), *_buf(d_ws), _stream(stream)),

@@ -286,3 +286,21 @@ def test_nemotron_layer_vs_torch(nm_weights_full):
     ref = y + TF.linear(TF.gelu(TF.linear(h2, _t(w[p + "w1"]), _t(w[p + "b1"]))),
                         _t(w[p + "w2"]), _t(w[p + "b2"]))
     assert np.abs(got - ref.numpy()).max() < 1e-11
+
+
+def test_nemotron_output_pooling_definition():
+    """Output frames of r x 10 ms: the mean of r consecutive 10 ms frames,
+    checked against an explicit loop; r = 1 is the identity; a constant track
+    stays constant; the mean over the clip is unchanged."""
+    rng = np.random.default_rng(14)
+    p = rng.random((8 * 7, 8))
+    assert np.array_equal(NM.pool_output(p, 1), p)
+    for r in (2, 4, 8):
+        got = NM.pool_output(p, r)
+        ref = np.array([[sum(p[r * k + q, s] for q in range(r)) / r for s in range(8)]
+                        for k in range(p.shape[0] // r)])
+        assert got.shape == (p.shape[0] // r, 8) and np.abs(got - ref).max() < 1e-15
+        assert abs(got.mean() - p.mean()) < 1e-15
+        assert np.allclose(NM.pool_output(np.full((16, 8), 0.3), r), 0.3)
+    with pytest.raises(ValueError):
+        NM.pool_output(p, 3)
