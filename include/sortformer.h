@@ -227,8 +227,9 @@ sf_status sortformer_stream_create(sf_model* model, const sf_stream_config* scfg
  * captured, since a replay may still be queued). */
 void sortformer_stream_destroy(sf_stream* st);
 /* Empty the cache/FIFO/audio history and every counter, for a new recording
- * (the runner's "streaming feed, reset, and final-flush" duties, ExecuTorch
- * issue, Proposed scope); enqueued on stream. */
+ * (a runner duty the ExecuTorch issue lists in its Proposed scope, beside
+ * feeding audio as it arrives and flushing the last chunk); enqueued on
+ * stream. */
 sf_status sortformer_stream_reset(sf_stream* st, void* stream);
 
 /* Samples per stream the next non-final step needs (like the Transformers
@@ -280,9 +281,10 @@ sf_status sortformer_stream_step_noalloc(sf_stream* st, const float* d_audio_new
                                          int32_t is_last, float* d_probs_out,
                                          int32_t* n_emitted_host, void* stream);
 
-/* Streaming feed of any sample count (the runner's "streaming feed, reset,
- * and final-flush", ExecuTorch issue, Proposed scope; the Transformers
- * streaming loop, which hands the processor audio as it arrives): the n_new
+/* Streaming feed of any sample count (the runner duties of the ExecuTorch
+ * issue's Proposed scope: feed audio as it arrives, reset, flush the last
+ * chunk; the Transformers streaming loop, which hands the processor audio as
+ * it arrives): the n_new
  * samples per stream (d_audio_new (B, n_new)) are appended to the samples
  * already pending, every step whose audio is then complete runs exactly as
  * sortformer_stream_step would run it, and the rest stays pending in the

@@ -1,8 +1,9 @@
 """GPU checks of the boundary's stream-state calls: the model metadata, full
 checkpoint / resume (NeMo API docs, SortformerStreamingState; Transformers
 speaker_cache), the streaming feed of arbitrary sample counts and the final
-flush (ExecuTorch issue, Proposed scope: "streaming feed, reset, and
-final-flush"), and the refusals that keep a stream's counters consistent."""
+flush (ExecuTorch issue, Proposed scope: the runner feeds audio as it comes,
+resets between recordings and flushes the last chunk), and the refusals that
+keep a stream's counters consistent."""
 import numpy as np
 import pytest
 import torch
