@@ -184,8 +184,12 @@ size_t sortformer_offline_workspace_bytes(const sf_model* model, int32_t batch,
 /* Offline forward (NeMo SortformerEncLabelModel.forward: audio -> per-frame
  * sigmoid speaker activity).
  *  d_audio: (B, N) fp32 16 kHz mono. d_probs: (B, n_out, S) fp32 output.
- *  SORTFORMER: n_out = ceil(floor(N/160)/8) frames of 80 ms; needs
- *    n_out <= SF_MAX_WINDOW (the whole clip is one encoder window).
+ *  SORTFORMER: n_out = ceil(floor(N/160)/8) frames of 80 ms. A clip of at
+ *    most SF_MAX_WINDOW encoder frames (81.9 s) is one encoder window; a
+ *    longer one is processed in the 'very high' streaming configuration's
+ *    chunks (340 frames + 40 look-ahead, FIFO 40, cache 188) on the
+ *    known-length schedule, as the Nemotron-style variant processes its
+ *    offline input in chunks; any N.
  *  NEMOTRON: the clip is processed in 30.4 s chunks with the arrival-order
  *    speaker cache and FIFO ("nemotron_offline" preset) and n_out =
  *    (8/stride)*ceil(floor(N/160)/8) frames of stride x 10 ms

@@ -18,9 +18,23 @@ def pre_encode_all(w, mel, block: int = 64):
     return np.concatenate(out) if out else np.zeros((0, sortformer.D_FC))
 
 
+# Longest clip (encoder frames) the offline forward takes as one window.
+MAX_WINDOW = 1024
+
+
 def sortformer_offline(audio, w):
+    """Offline forward. A clip of at most MAX_WINDOW encoder frames is one
+    window. Reading for longer clips (the pages' Sortformer offline forward has
+    no stated limit, and the Nemotron-style variant processes long offline
+    input in chunks with its cache and FIFO): the 'very high' streaming
+    configuration on the known-length schedule."""
     mel = frontend.log_mel(audio)
-    return sortformer.encode_window(w, pre_encode_all(w, mel))
+    emb = pre_encode_all(w, mel)
+    if emb.shape[0] <= MAX_WINDOW:
+        return sortformer.encode_window(w, emb)
+    p, _ = streaming.run_stream(emb, streaming.StreamConfig.preset("very_high"),
+                                sortformer_encoder(w), 4)
+    return p
 
 
 def sortformer_encoder(w):

@@ -373,8 +373,12 @@ size_t sortformer_offline_workspace_bytes(const sf_model* m, int32_t B, int64_t 
   if (!m || B < 1 || N < 0) return 0;
   const int Te = frames_of(N);
   if (m->cfg.arch == SF_ARCH_SORTFORMER) {
-    if (Te > SF_MAX_WINDOW) return 0;
-    return al256(enc_ws_bytes(m, B, std::max(Te, 1))) + al256(pre_ws_bytes(m, B, Te));
+    if (Te <= SF_MAX_WINDOW)
+      return al256(enc_ws_bytes(m, B, std::max(Te, 1))) + al256(pre_ws_bytes(m, B, Te));
+    sf_stream_config c{};  // longer clips: 'very high' chunks, pre-encoded per chunk
+    sortformer_stream_preset("very_high", &c);
+    return al256(pre_ws_bytes(m, B, c.chunk_len + c.right_context)) +
+           al256(state_layout(m, &c, B).total) + al256(enc_ws_bytes(m, B, stream_cap(&c)));
   }
   sf_stream_config c{};
   sortformer_stream_preset("nemotron_offline", &c);
@@ -392,6 +396,41 @@ sf_status sortformer_forward_offline(sf_model* m, const float* d_audio, int32_t 
   const hipStream_t s = HS(stream);
   const int T = (int)(N / 160), Te = frames_of(N), S = m->cfg.n_spk;
   char* p = static_cast<char*>(d_ws);
+  if (m->cfg.arch == SF_ARCH_SORTFORMER && Te > SF_MAX_WINDOW) {
+    // longer than one encoder window: the 'very high' configuration's chunks
+    // (340 frames + 40 look-ahead) with the speaker cache and FIFO, on the
+    // known-length schedule; each chunk is pre-encoded from the clip when it
+    // enters the window
+    *n_out = Te;
+    sf_stream st{};
+    st.m = m;
+    sortformer_stream_preset("very_high", &st.sc);
+    st.B = B; st.S = S; st.D = 512;
+    st.use_graphs = false;
+    st.cap_stream = nullptr;
+    st.cap = stream_cap(&st.sc);
+    st.ring_cap = ring_cap_for(&st.sc);
+    const int L = st.sc.chunk_len, R = st.sc.right_context;
+    char* pre = p;
+    p += al256(pre_ws_bytes(m, B, L + R));
+    bind_state(&st, p);
+    p += al256(state_layout(m, &st.sc, B).total);
+    EncWs enc = carve_enc(m, p, B, st.cap);
+    reset_host(&st);
+    reset_device(&st, s);
+    for (int c0 = 0; c0 < Te; c0 += L) {
+      const int c1 = std::min(Te, c0 + L);
+      const int rc = c1 == Te ? 0 : std::min(R, Te - c1);
+      const int e1 = c1 + rc;
+      pre_encode_range(m, d_audio, N, -1, N, T, st.enc_done, e1, B,
+                       st.E[st.cur] + (size_t)(st.Lc + st.Lf + st.Lp) * 512,
+                       (long long)st.cap * 512, pre, s);
+      st.Lp += e1 - st.enc_done;
+      st.enc_done = e1;
+      step_core(&st, c1 - c0, d_probs + (size_t)c0 * S, (long long)Te * S, enc, nullptr, s);
+    }
+    return launched();
+  }
   if (m->cfg.arch == SF_ARCH_SORTFORMER) {
     *n_out = Te;
     if (Te == 0) return SF_OK;

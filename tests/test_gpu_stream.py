@@ -299,3 +299,20 @@ def test_graph_replays_match_direct_launches(rt, sf, sfbf):
     for rep in range(2):
         b.reset()
         assert np.array_equal(b.run(a3).cpu().numpy(), r3), f"batched replay {rep}"
+
+
+def test_sortformer_offline_beyond_one_window(rt, sfbf):
+    """A 100 s clip (1250 encoder frames, past the 1024-frame single window)
+    runs in 'very high' chunks: two clips batched against the oracle's
+    chunked offline forward at the bf16 bar, and the batch against each clip
+    run alone, bit for bit."""
+    w = make_weights("sortformer", 0, bf16=True)
+    clips = [meeting_audio(100.0, 4, 600 + i) for i in range(2)]
+    got = sfbf.offline(_cuda(np.stack(clips))).cpu().numpy()
+    assert got.shape == (2, 1250, 4)
+    ref = OR.sortformer_offline(clips[0], w)
+    err, agree = _report("offline 100 s bf16 (chunked)", got[0], ref)
+    assert err <= 2e-2 and agree >= 0.995
+    for i in range(2):
+        one = sfbf.offline(_cuda(clips[i])[None])[0].cpu().numpy()
+        assert np.array_equal(one, got[i])
