@@ -40,6 +40,7 @@ struct ConfLayer {
 struct TfLayer {
   const void *wqkv, *wo, *w1, *w2;
   const void *wo_f, *w1_f, *w2_f;  // bf16 fragment-major copies (fused layer tail)
+  const void* wqkv_f;               // bf16 fragment-major Q/K/V (batched layer tail)
   const float *bqkv, *bo, *b1, *b2, *ln1_g, *ln1_b, *ln2_g, *ln2_b;
 };
 

@@ -110,11 +110,16 @@ int tf_tail(const TfTailArgs& a, hipStream_t s);
 //   x1 = LN1(x + ctx Wo^T + bo); xo = LN2(x1 + relu(x1 W1^T + b1) W2^T + b2)
 // and h = bf16(xo), the next layer's GEMM operand. xo may alias x (each
 // workgroup reads its rows before writing them). wo, w1, w2 fragment-major.
+// With wqkv (fragment-major [576][192]) the next layer's Q/K/V projection of
+// xo follows in the same kernel: Q and K row-major into qkv (576 columns), V
+// transposed per head into vt[((b*8 + head)*24 + d)*vpitch + w] for row
+// m = b*vrows + w; h may then be null (not written).
 struct TfLayerArgs {
   const void* ctx; const float* x; float* xo; void* h; int M;
   const void* wo; const float* bo; const float* g1; const float* be1;
   const void* w1; const float* b1; const void* w2; const float* b2;
   const float* g2; const float* be2;
+  const void* wqkv; const float* bqkv; void* qkv; void* vt; int vrows, vpitch;
 };
 void tf_layer_tp(const TfLayerArgs& a, hipStream_t s);
 

@@ -272,6 +272,7 @@ void build_sortformer(sf_model* m, Arena& A, const Src& s) {
       L.wo_f = A.frag(s.get(p + "wo"), 192, 192);
       L.w1_f = A.frag(s.get(p + "w1"), 768, 192);
       L.w2_f = A.frag(s.get(p + "w2"), 192, 768);
+      L.wqkv_f = A.frag(have ? w.data() : nullptr, 576, 192);
     }
   }
   {
@@ -683,10 +684,13 @@ static void encode_sortformer(const sf_model* m, EncWs& w, int B, int W, int n_v
   // encoder_proj: fp32 residual stream of the transformer + GEMM operand
   c.lin(w.h, 512, m->proj_w, m->proj_b, 192, 512, w.ctx, 192, EPI_STORE, bf, w.x, 192);
   const void* hin = w.ctx;
+  // batched bf16 windows: each layer's tail kernel also projects the next
+  // layer's Q/K/V, so only the first layer runs the Q/K/V GEMM
+  const bool tail_qkv = bf && B * W > SLICE_MAX_ROWS;
   for (int l = 0; l < 18; ++l) {
     const TfLayer& L = m->tf[l];
     tp.at(17 + l, SF_TAP_LAYER_IN, w.x, false, 192);
-    c.qkv(hin, 192, L.wqkv, L.bqkv, w.big, 24, W);
+    if (!tail_qkv || l == 0) c.qkv(hin, 192, L.wqkv, L.bqkv, w.big, 24, W);
     AttnArgs a{};
     a.qkv = w.big; a.ldq = 576; a.qoff = 0; a.koff = 192; a.vt = w.vt; a.vpitch = w.vpitch;
     a.B = B; a.H = 8; a.W = W; a.n_valid = n_valid; a.nv = nv;
@@ -712,6 +716,12 @@ static void encode_sortformer(const sf_model* m, EncWs& w, int B, int W, int n_v
       t.ctx = w.ctx; t.x = w.x; t.xo = w.x; t.h = w.h; t.M = B * W;
       t.wo = L.wo_f; t.bo = L.bo; t.g1 = L.ln1_g; t.be1 = L.ln1_b;
       t.w1 = L.w1_f; t.b1 = L.b1; t.w2 = L.w2_f; t.b2 = L.b2; t.g2 = L.ln2_g; t.be2 = L.ln2_b;
+      if (l < 17) {  // the next layer's Q/K/V from the same kernel; h is not needed then
+        const TfLayer& N = m->tf[l + 1];
+        t.h = nullptr;
+        t.wqkv = N.wqkv_f; t.bqkv = N.bqkv; t.qkv = w.big; t.vt = w.vt;
+        t.vrows = W; t.vpitch = w.vpitch;
+      }
       tf_layer_tp(t, s);
     } else {
       int ns = c.branch(w.ctx, 192, L.wo, 192, 192);

@@ -380,26 +380,97 @@ void tf_layer_tp_kernel(TfLayerArgs a) {
   }
   layernorm(xv, a.g2, a.be2);
   bf16_t* h = static_cast<bf16_t*>(a.h);
+  int gq = g;  // opaque copy: row indices recomputed, not kept from the x loads
+  asm volatile("" : "+v"(gq));
 #pragma unroll
   for (int rt = 0; rt < TB_RT; ++rt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = r0 + 16 * rt + 4 * g + r;
+      const int row = r0 + 16 * rt + 4 * gq + r;
       if (row >= a.M) continue;
 #pragma unroll
       for (int ct = 0; ct < TB_CT; ++ct) {
         const int col = 48 * w + 16 * ct + c16;
+        const bf16_t hv = f2bf(xv[rt][ct][r]);
         a.xo[(size_t)row * TD + col] = xv[rt][ct][r];
-        h[(size_t)row * TD + col] = f2bf(xv[rt][ct][r]);
+        if (h) h[(size_t)row * TD + col] = hv;
+        // the next layer's Q/K/V operand (As is free: the chunk loop ended
+        // with a barrier after its last read)
+        As[(16 * rt + 4 * g + r) * TLH + col] = hv;
       }
     }
+  if (!a.wqkv) return;
+
+  // ---- the next layer's Q/K/V projection of xo: pass p = 0, 1, 2 forms the
+  // 192 columns of Q, K, V (wave w: column tiles 3w .. 3w+2 of the pass),
+  // stages them in Hs as bf16 and stores them with 16-byte writes: Q and K
+  // row-major (576 per row), V transposed per head (head dim 24, window rows
+  // along the pitch). Rows of As past M hold finite values of a clamped row;
+  // their outputs are not stored.
+  __syncthreads();
+  // an opaque copy of the thread index: the store indexing below is then
+  // recomputed here rather than kept live (and spilled) from the ctx loads
+  int tq = tid;
+  asm volatile("" : "+v"(tq));
+  bf16_t* qkv = static_cast<bf16_t*>(a.qkv);
+  bf16_t* vt = static_cast<bf16_t*>(a.vt);
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    zero();
+    product(As, a.wqkv, TD, 12 * pass + 3 * w, 0);
+#pragma unroll
+    for (int ct = 0; ct < TB_CT; ++ct) {
+      const int col = 48 * w + 16 * ct + c16;
+      const float bq = a.bqkv[TD * pass + col];
+#pragma unroll
+      for (int rt = 0; rt < TB_RT; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          Hs[(16 * rt + 4 * g + r) * TLH + col] = f2bf(acc[rt][ct][r] + bq);
+    }
+    __syncthreads();
+    if (pass < 2) {
+      constexpr int CPR = TD / 8;
+#pragma unroll
+      for (int i = 0; i < TB_RB * CPR / 256; ++i) {
+        const int c = tq + 256 * i, r = c / CPR, q = c % CPR, row = r0 + r;
+        if (row < a.M)
+          *reinterpret_cast<vec16*>(qkv + (size_t)row * (3 * TD) + TD * pass + 8 * q) =
+              *reinterpret_cast<const vec16*>(&Hs[r * TLH + 8 * q]);
+      }
+    } else {
+      // 8-row runs of one V column: 192 columns x 8 runs
+#pragma unroll 1
+      for (int i = 0; i < TD * (TB_RB / 8) / 256; ++i) {
+        const int c = tq + 256 * i, col = c >> 3, r = (c & 7) * 8, row = r0 + r;
+        if (row >= a.M) continue;
+        const int hh = col / 24, d = col % 24, bb = row / a.vrows, wp = row % a.vrows;
+        bf16_t* dst = vt + ((size_t)(bb * 8 + hh) * 24 + d) * a.vpitch + wp;
+        if (row + 8 <= a.M && wp + 8 <= a.vrows && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+          vec16 v;
+          bf16_t* pv = reinterpret_cast<bf16_t*>(&v);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pv[e] = Hs[(r + e) * TLH + col];
+          *reinterpret_cast<vec16*>(dst) = v;
+        } else {
+          for (int e = 0; e < 8 && row + e < a.M; ++e) {
+            const int b2 = (row + e) / a.vrows, w2 = (row + e) % a.vrows;
+            vt[((size_t)(b2 * 8 + hh) * 24 + d) * a.vpitch + w2] = Hs[(r + e) * TLH + col];
+          }
+        }
+      }
+    }
+    __syncthreads();  // the next pass rewrites Hs
+  }
 }
 
 void tf_layer_tp(const TfLayerArgs& a, hipStream_t s) {
   if (a.M <= 0) return;
   const double M = a.M;
-  klaunch(PROF_GEMM, 2.0 * M * TD * TD + 4.0 * M * TD * TF,
-          2.0 * M * TD + 4.0 * M * TD * 2 + 2.0 * (TD * TD + 2.0 * TD * TF) + 2.0 * M * TD,
+  const bool q = a.wqkv != nullptr;
+  klaunch(PROF_GEMM, 2.0 * M * TD * TD + 4.0 * M * TD * TF + (q ? 2.0 * M * TD * 3 * TD : 0.0),
+          2.0 * M * TD + 4.0 * M * TD * 2 + 2.0 * (TD * TD + 2.0 * TD * TF) +
+              (q ? 2.0 * M * 3 * TD + 2.0 * 3 * TD * TD : 2.0 * M * TD),
           tf_layer_tp_kernel, dim3((a.M + TB_RB - 1) / TB_RB), dim3(256), s, a);
 }
 
