@@ -144,6 +144,45 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, const float* cs, i
     if (n0 >= g.vcol) {  // V block: column c of the tile is one (head, dim) row of V^T
       OutT* vt = static_cast<OutT*>(g.vt);
       const int H = (g.N - g.vcol) / g.vhd;
+      if (g.vrows >= BM) {
+        // The tile's rows fall in at most two windows, A = m0 / vrows and A+1.
+        // Keys are written in groups of 8 aligned to the window's own key
+        // index w (a window of vrows % 8 != 0 rows starts off the tile's
+        // 8-row grid): whole groups as vectors, the group cut by the tile's
+        // edge or the window's end element by element. Within a wave, 16
+        // columns x 4 consecutive groups.
+        const int W = g.vrows, m1 = min(m0 + BM, g.M);
+        const int bA = m0 / W, loA = m0 - bA * W, hiA = min(m1 - bA * W, W);
+        const int gA0 = loA >> 3, nA = ((hiA - 1) >> 3) - gA0 + 1;
+        const int hiB = m1 - (bA + 1) * W;  // rows of window A+1 in the tile
+        const int nG = nA + (hiB > 0 ? ((hiB - 1) >> 3) + 1 : 0);
+        constexpr int NG = (BM / 8 + 2 + 3) / 4 * 4;  // bound on groups per tile
+        static_assert(C % 16 == 0, "V tile columns");
+        for (int q = tid; q < C * NG; q += 256) {
+          const int c = (q / 64) % (C / 16) * 16 + (q & 15);
+          const int gi = (q / 64) / (C / 16) * 4 + ((q >> 4) & 3);
+          if (gi >= nG) continue;
+          const bool inA = gi < nA;
+          const int bb = inA ? bA : bA + 1, grp = inA ? gA0 + gi : gi - nA;
+          const int lo = inA ? loA : 0, hi = inA ? hiA : hiB;
+          const int w0 = grp * 8, ws = max(w0, lo), we = min(w0 + 8, hi);
+          const int rb = bb * W - m0;  // tile row of key 0 of window bb
+          const int nn = n0 + c - g.vcol, hh = nn / g.vhd, d = nn % g.vhd;
+          OutT* dst = vt + ((size_t)(bb * H + hh) * g.vhd + d) * g.vpitch + w0;
+          if (ws == w0 && we == w0 + 8 && aligned16(dst)) {
+#pragma unroll
+            for (int e0 = 0; e0 < 8; e0 += E) {
+              float v[E];
+#pragma unroll
+              for (int e = 0; e < E; ++e) v[e] = cs[(rb + w0 + e0 + e) * LDC + c];
+              OutVec<OutT>::put(dst + e0, v);
+            }
+          } else {
+            for (int w = ws; w < we; ++w) dst[w - w0] = from_f<OutT>(cs[(rb + w) * LDC + c]);
+          }
+        }
+        return;
+      }
       for (int q = tid; q < BM / E * C; q += 256) {
         const int c = q / (BM / E), r = (q % (BM / E)) * E, m = m0 + r;
         if (m >= g.M) continue;

@@ -438,25 +438,49 @@ void tf_layer_tp_kernel(TfLayerArgs a) {
           *reinterpret_cast<vec16*>(qkv + (size_t)row * (3 * TD) + TD * pass + 8 * q) =
               *reinterpret_cast<const vec16*>(&Hs[r * TLH + 8 * q]);
       }
+    } else if (a.vrows >= TB_RB) {
+      // V^T: the block's rows fall in at most two windows, A and A+1; keys
+      // go out in groups of 8 aligned to the window's own key index (whole
+      // groups as 16-byte vectors, groups cut by the block edge or the
+      // window's end element by element). A wave: 16 columns x 4 groups.
+      const int W = a.vrows, m1 = min(r0 + TB_RB, a.M);
+      const int bA = r0 / W, loA = r0 - bA * W, hiA = min(m1 - bA * W, W);
+      const int gA0 = loA >> 3, nA = ((hiA - 1) >> 3) - gA0 + 1;
+      const int hiB = m1 - (bA + 1) * W;
+      const int nG = nA + (hiB > 0 ? ((hiB - 1) >> 3) + 1 : 0);
+      constexpr int NG = (TB_RB / 8 + 2 + 3) / 4 * 4;
+#pragma unroll 1
+      for (int qi = tq; qi < TD * NG; qi += 256) {
+        const int col = (qi / 64) % (TD / 16) * 16 + (qi & 15);
+        const int gi = (qi / 64) / (TD / 16) * 4 + ((qi >> 4) & 3);
+        if (gi >= nG) continue;
+        const bool inA = gi < nA;
+        const int bb = inA ? bA : bA + 1, grp = inA ? gA0 + gi : gi - nA;
+        const int lo = inA ? loA : 0, hi = inA ? hiA : hiB;
+        const int w0 = grp * 8, ws = max(w0, lo), we = min(w0 + 8, hi);
+        const int rb = bb * W - r0;  // block row of key 0 of window bb
+        const int hh = col / 24, d = col % 24;
+        bf16_t* dst = vt + ((size_t)(bb * 8 + hh) * 24 + d) * a.vpitch + w0;
+        if (ws == w0 && we == w0 + 8 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+          vec16 v;
+          bf16_t* pv = reinterpret_cast<bf16_t*>(&v);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pv[e] = Hs[(rb + w0 + e) * TLH + col];
+          *reinterpret_cast<vec16*>(dst) = v;
+        } else {
+          for (int w = ws; w < we; ++w) dst[w - w0] = Hs[(rb + w) * TLH + col];
+        }
+      }
     } else {
-      // 8-row runs of one V column: 192 columns x 8 runs
+      // windows shorter than the block: 8-row runs of one V column
 #pragma unroll 1
       for (int i = 0; i < TD * (TB_RB / 8) / 256; ++i) {
         const int c = tq + 256 * i, col = c >> 3, r = (c & 7) * 8, row = r0 + r;
         if (row >= a.M) continue;
-        const int hh = col / 24, d = col % 24, bb = row / a.vrows, wp = row % a.vrows;
-        bf16_t* dst = vt + ((size_t)(bb * 8 + hh) * 24 + d) * a.vpitch + wp;
-        if (row + 8 <= a.M && wp + 8 <= a.vrows && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
-          vec16 v;
-          bf16_t* pv = reinterpret_cast<bf16_t*>(&v);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pv[e] = Hs[(r + e) * TLH + col];
-          *reinterpret_cast<vec16*>(dst) = v;
-        } else {
-          for (int e = 0; e < 8 && row + e < a.M; ++e) {
-            const int b2 = (row + e) / a.vrows, w2 = (row + e) % a.vrows;
-            vt[((size_t)(b2 * 8 + hh) * 24 + d) * a.vpitch + w2] = Hs[(r + e) * TLH + col];
-          }
+        const int hh = col / 24, d = col % 24;
+        for (int e = 0; e < 8 && row + e < a.M; ++e) {
+          const int b2 = (row + e) / a.vrows, w2 = (row + e) % a.vrows;
+          vt[((size_t)(b2 * 8 + hh) * 24 + d) * a.vpitch + w2] = Hs[(r + e) * TLH + col];
         }
       }
     }
