@@ -525,6 +525,38 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs g) {
         for (int j = 0; j < TN; ++j) acc[i][j] = M_::mma(af[i], bfr[j], acc[i][j]);
     }
   }
+  if constexpr (EPI == EPI_RESID) {
+    // the residual rows this thread updates, requested before the staging so
+    // that they land while it runs
+    constexpr int NQ = BM * BN / 4 / 256;
+    float4 xr[NQ];
+    float* x = static_cast<float*>(g.out);
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int q = tid + 256 * i, r = q / (BN / 4), c = (q % (BN / 4)) * 4;
+      const int m = min(m0 + r, g.M - 1);
+      xr[i] = *reinterpret_cast<const float4*>(x + (size_t)m * g.ldo + n0 + c);
+    }
+    __syncthreads();  // the ring is reused for the staged epilogue
+    float* cs = reinterpret_cast<float*>(smem);
+    stage_tile<EPI, BN, TM, TN>(g, acc, cs, n0, wm * 64, wn * (BN / 2), lane);
+    __syncthreads();
+    constexpr int LDC = BN + 4;
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int q = tid + 256 * i, r = q / (BN / 4), c = (q % (BN / 4)) * 4, m = m0 + r;
+      if (m < g.M) {
+        const float4 t = *reinterpret_cast<const float4*>(cs + r * LDC + c);
+        float4 v = xr[i];
+        v.x += g.ralpha * t.x;
+        v.y += g.ralpha * t.y;
+        v.z += g.ralpha * t.z;
+        v.w += g.ralpha * t.w;
+        *reinterpret_cast<float4*>(x + (size_t)m * g.ldo + n0 + c) = v;
+      }
+    }
+    return;
+  }
   __syncthreads();  // the ring is reused for the staged epilogue
   float* cs = reinterpret_cast<float*>(smem);
   stage_tile<EPI, BN, TM, TN>(g, acc, cs, n0, wm * 64, wn * (BN / 2), lane);
@@ -846,6 +878,15 @@ int gemm_glu_dwconv(const GemmArgs& g, hipStream_t s) {
   g_bytes = 2.0 * g.M * g.K + 2.0 * g.N * g.K + 2.0 * g.M * (g.N / 2);
   klaunch(PROF_GEMM, g_flops, g_bytes, gemm_slice_dma_kernel<bf16_t, EPI_GLU, 512, 32, true>,
           dim3(g.N / 64, (g.M + 23) / 24, 1), dim3(256), s, g);
+  return 1;
+}
+
+int gemm_resid(const GemmArgs& g, hipStream_t s) {
+  if (g.M <= SLICE_MAX_ROWS || g.K % SF_BIG_BK || g.N % 128 || g.K <= 0) return -1;
+  klaunch(PROF_GEMM, 2.0 * g.M * g.N * g.K,
+          2.0 * ((double)g.M * g.K + (double)g.N * g.K) + 8.0 * g.M * g.N,
+          gemm_big_kernel<float, EPI_RESID, 128, SF_BIG_BK, SF_BIG_NST>,
+          dim3(g.N / 128, (g.M + 127) / 128), dim3(256), s, g);
   return 1;
 }
 

@@ -9,7 +9,7 @@
 namespace sf {
 
 enum { EPI_STORE = 0, EPI_SWISH = 1, EPI_RELU = 2, EPI_GELU = 3, EPI_GLU = 5, EPI_PARTIAL = 6,
-       EPI_QKV = 7 };
+       EPI_QKV = 7, EPI_RESID = 8 };
 // Windows up to this many rows use the K-slice GEMM kernel.
 #define SLICE_MAX_ROWS 4096
 // fp32 partial-sum scratch per GEMM row: slices * N never exceeds this
@@ -37,10 +37,16 @@ struct GemmArgs {
   const float* dw_w9; const float* dw_sc; const float* dw_sh;
   int dw_W, dw_nvalid;
   const int* dw_nv;  // when non-null: device copy of the valid frame count, read instead
+  float ralpha;      // gemm_resid: out (fp32) += ralpha * (A W^T + bias)
 };
 // EPI_PARTIAL writes fp32 partial sums (no bias) to out as [slice][M][N] and
 // returns the slice count; other epilogues return 1.
 int gemm(const GemmArgs& g, int epi, bool bf16_in, bool bf16_out, hipStream_t s);
+// Residual branch of batched windows (bf16 A and W, more than 4096 rows,
+// K % 64 == 0, N % 128 == 0): out (fp32, ldo) += ralpha * (A W^T + bias), in
+// place, with the arithmetic of a LayerNorm that folds in one partial slice.
+// Returns 1, or -1 (nothing launched) for other shapes.
+int gemm_resid(const GemmArgs& g, hipStream_t s);
 // Pointwise-1 of the conformer convolution module (bf16, N = 1024 GLU
 // interleaved, K = 512) with the GLU, the depthwise conv (k = 9), the folded
 // BatchNorm and the Swish fused into its epilogue: out (M, 512) bf16. Each

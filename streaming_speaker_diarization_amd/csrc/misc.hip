@@ -146,11 +146,12 @@ void layernorm(const LnArgs& a, bool bf16, hipStream_t s) {
 // ------------------------------------------- conformer depthwise conv (k=9)
 // out[t,c] = swish(scale[c] * sum_k w[c,k] g[t+k-4,c] + shift[c]); rows at or
 // beyond n_valid (and outside the window) count as zero. BatchNorm and the
-// conv bias are folded into scale/shift. One workgroup = DW_ROWS frames of
-// one stream; a thread owns 4 channels and keeps the DW_ROWS + 8 input rows
-// of them in registers (16-byte loads, each input row loaded once).
-#define DW_ROWS 4
-template <typename T>
+// conv bias are folded into scale/shift. One workgroup = R frames of one
+// stream; a thread owns 4 channels and keeps the R + 8 input rows of them in
+// registers (16-byte loads, each input row loaded once). R = 4 for one or a
+// few windows (enough workgroups to fill the chip), 16 for batched windows
+// (1.5 rows read per row written instead of 3).
+template <typename T, int R>
 __global__ __launch_bounds__(128) void dwconv_time_kernel(const float* glu, int W, int n_valid_h,
                                                           const int* nv, const float* w9,
                                                           const float* sc, const float* sh, T* out) {
@@ -164,14 +165,14 @@ __global__ __launch_bounds__(128) void dwconv_time_kernel(const float* glu, int 
     const int pid = blockIdx.x + gx * blockIdx.y;
     const int q8 = total / 8, r8 = total % 8, xcd = pid % 8;
     const int t = xcd * q8 + min(xcd, r8) + pid / 8;
-    t0 = (t % gx) * DW_ROWS;
+    t0 = (t % gx) * R;
     b = t / gx;
   }
   const int c = threadIdx.x * 4;
   const float* gb = glu + (size_t)b * W * 512 + c;
-  float4 x[DW_ROWS + 8];
+  float4 x[R + 8];
 #pragma unroll
-  for (int j = 0; j < DW_ROWS + 8; ++j)
+  for (int j = 0; j < R + 8; ++j)
     x[j] = *reinterpret_cast<const float4*>(gb + (size_t)min(max(t0 + j - 4, 0), W - 1) * 512);
   float4 wk[9];  // w[c..c+3][k] for tap k, from the [c][9] layout
   {
@@ -187,7 +188,7 @@ __global__ __launch_bounds__(128) void dwconv_time_kernel(const float* glu, int 
   const float4 s4 = *reinterpret_cast<const float4*>(sc + c);
   const float4 h4 = *reinterpret_cast<const float4*>(sh + c);
 #pragma unroll
-  for (int r = 0; r < DW_ROWS; ++r) {
+  for (int r = 0; r < R; ++r) {
     const int t = t0 + r;
     if (t >= W) break;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -219,13 +220,18 @@ void dwconv_time(const float* glu, int B, int W, int n_valid, const int* nv, con
                  const float* sc, const float* sh, void* out, bool bf16, hipStream_t s) {
   if (W <= 0) return;
   const double fl = 2.0 * 9 * 512 * B * W, by = (double)B * W * 512 * (4.0 + (bf16 ? 2 : 4));
-  dim3 grid((W + DW_ROWS - 1) / DW_ROWS, B);
-  if (bf16)
-    klaunch(PROF_CONV, fl, by, dwconv_time_kernel<bf16_t>, grid, dim3(128), s, glu, W, n_valid, nv,
-            w9, sc, sh, static_cast<bf16_t*>(out));
-  else
-    klaunch(PROF_CONV, fl, by, dwconv_time_kernel<float>, grid, dim3(128), s, glu, W, n_valid, nv,
-            w9, sc, sh, static_cast<float*>(out));
+  auto go = [&](auto rows) {
+    constexpr int R = decltype(rows)::value;
+    dim3 grid((W + R - 1) / R, B);
+    if (bf16)
+      klaunch(PROF_CONV, fl, by, dwconv_time_kernel<bf16_t, R>, grid, dim3(128), s, glu, W, n_valid,
+              nv, w9, sc, sh, static_cast<bf16_t*>(out));
+    else
+      klaunch(PROF_CONV, fl, by, dwconv_time_kernel<float, R>, grid, dim3(128), s, glu, W, n_valid,
+              nv, w9, sc, sh, static_cast<float*>(out));
+  };
+  if ((size_t)B * W > 4096) go(std::integral_constant<int, 16>{});
+  else go(std::integral_constant<int, 4>{});
 }
 
 // ------------------------------------------------------------ log-mel

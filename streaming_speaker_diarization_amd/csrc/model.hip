@@ -592,6 +592,25 @@ struct Ctx {
     g.out = w.part; g.ldo = N; g.max_split = (int)(w.part_floats / ((size_t)M * N));
     return gemm(g, EPI_PARTIAL, bf, false, s);
   }
+  // x += alpha * (A W^T + bias) (N = 512), then the LayerNorm(s) as in ln():
+  // batched bf16 windows add the branch in the GEMM's epilogue (x_mode 1,
+  // storing the updated residual, is then already done); otherwise the GEMM
+  // writes partial slices that the LayerNorm sums and adds
+  void branch_ln(const void* A, int lda, const void* W, int K, const float* bias, float alpha,
+                 const float* g1, const float* b1, const float* g2, const float* b2, int x_mode,
+                 void* y) {
+    if (bf && M > SLICE_MAX_ROWS) {
+      GemmArgs g{};
+      g.A = A; g.lda = lda; g.W = W; g.ldw = K; g.M = M; g.N = 512; g.K = K; g.bias = bias;
+      g.out = w.x; g.ldo = 512; g.ralpha = alpha;
+      if (gemm_resid(g, s) == 1) {
+        ln(512, 0, nullptr, 0.f, g1, b1, g2, b2, x_mode == 1 ? 0 : x_mode, y);
+        return;
+      }
+    }
+    const int ns = branch(A, lda, W, 512, K);
+    ln(512, ns, bias, alpha, g1, b1, g2, b2, x_mode, y);
+  }
   // LayerNorm(s) with the pending residual branch (ns partial slices) folded in.
   void ln(int D, int ns, const float* pbias, float alpha, const float* g1, const float* b1,
           const float* g2, const float* b2, int x_mode, void* y_act) {
@@ -634,8 +653,8 @@ static void encode_sortformer(const sf_model* m, EncWs& w, int B, int W, int n_v
     tp.at(l, SF_TAP_LAYER_IN, w.x, false, 512);
     // macaron FFN, first half: x += FF(LN(x))/2
     c.lin(w.h, 512, L.ff1_w1, L.ff1_b1, 2048, 512, w.big, 2048, EPI_SWISH, bf);
-    int ns = c.branch(w.big, 2048, L.ff1_w2, 512, 2048);
-    c.ln(512, ns, L.ff1_b2, 0.5f, L.att_g, L.att_b, nullptr, nullptr, 1, w.h);
+    c.branch_ln(w.big, 2048, L.ff1_w2, 2048, L.ff1_b2, 0.5f, L.att_g, L.att_b, nullptr, nullptr, 1,
+                w.h);
     // relative-position self-attention
     c.qkv(w.h, 512, L.wqkv, L.bqkv, w.big, 64, W);
     AttnArgs a{};
@@ -649,8 +668,8 @@ static void encode_sortformer(const sf_model* m, EncWs& w, int B, int W, int n_v
     if (fuse_wo) { a.wo_f = L.wo_f; a.part = w.part; a.M = B * W; }
     attention(a, ATT_RELPOS, 64, bf, s);
     tp.at(l, SF_TAP_ATTN_CTX, w.ctx, bf, 512);
-    ns = fuse_wo ? 8 : c.branch(w.ctx, 512, L.wo, 512, 512);
-    c.ln(512, ns, L.bo, 1.f, L.conv_g, L.conv_b, nullptr, nullptr, 1, w.h);
+    if (fuse_wo) c.ln(512, 8, L.bo, 1.f, L.conv_g, L.conv_b, nullptr, nullptr, 1, w.h);
+    else c.branch_ln(w.ctx, 512, L.wo, 512, L.bo, 1.f, L.conv_g, L.conv_b, nullptr, nullptr, 1, w.h);
     // convolution module
     if (bf && B * W <= SLICE_MAX_ROWS) {
       // pointwise-1, GLU, depthwise conv, BatchNorm and Swish in one kernel
@@ -661,23 +680,22 @@ static void encode_sortformer(const sf_model* m, EncWs& w, int B, int W, int n_v
       g.dw_w9 = L.dw9; g.dw_sc = L.dw_sc; g.dw_sh = L.dw_sh; g.dw_W = W; g.dw_nvalid = n_valid;
       g.dw_nv = nv;
       gemm_glu_dwconv(g, s);
-      ns = c.branch(w.ctx, 512, L.pw2, 512, 512);
+      c.branch_ln(w.ctx, 512, L.pw2, 512, L.pw2_b, 1.f, L.ff2_g, L.ff2_b, nullptr, nullptr, 1, w.h);
     } else {
       c.lin(w.h, 512, L.pw1, L.pw1_b, 1024, 512, w.glu, 512, EPI_GLU, false);
       dwconv_time(w.glu, B, W, n_valid, nv, L.dw9, L.dw_sc, L.dw_sh, w.h, bf, s);
-      ns = c.branch(w.h, 512, L.pw2, 512, 512);
+      c.branch_ln(w.h, 512, L.pw2, 512, L.pw2_b, 1.f, L.ff2_g, L.ff2_b, nullptr, nullptr, 1, w.h);
     }
-    c.ln(512, ns, L.pw2_b, 1.f, L.ff2_g, L.ff2_b, nullptr, nullptr, 1, w.h);
     // macaron FFN, second half, then the output LayerNorm (fused with the
     // next layer's first LayerNorm)
     c.lin(w.h, 512, L.ff2_w1, L.ff2_b1, 2048, 512, w.big, 2048, EPI_SWISH, bf);
-    ns = c.branch(w.big, 2048, L.ff2_w2, 512, 2048);
     if (l < 16) {
-      c.ln(512, ns, L.ff2_b2, 0.5f, L.out_g, L.out_b, m->conf[l + 1].ff1_g, m->conf[l + 1].ff1_b,
-           2, w.h);
+      c.branch_ln(w.big, 2048, L.ff2_w2, 2048, L.ff2_b2, 0.5f, L.out_g, L.out_b,
+                  m->conf[l + 1].ff1_g, m->conf[l + 1].ff1_b, 2, w.h);
       tp.at(l, SF_TAP_LAYER_OUT, w.x, false, 512);
     } else {
-      c.ln(512, ns, L.ff2_b2, 0.5f, L.out_g, L.out_b, nullptr, nullptr, 0, w.h);
+      c.branch_ln(w.big, 2048, L.ff2_w2, 2048, L.ff2_b2, 0.5f, L.out_g, L.out_b, nullptr, nullptr,
+                  0, w.h);
       tp.at(l, SF_TAP_LAYER_OUT, w.h, bf, 512);
     }
   }
@@ -753,14 +771,16 @@ static void encode_nemotron(const sf_model* m, EncWs& w, int B, int W, int n_val
     if (fuse_wo) { a.wo_f = L.wo_f; a.part = w.part; a.M = B * W; }
     attention(a, ATT_ROPE, 64, bf, s);
     tp.at(l, SF_TAP_ATTN_CTX, w.ctx, bf, 512);
-    int ns = fuse_wo ? 8 : c.branch(w.ctx, 512, L.wo, 512, 512);
-    c.ln(512, ns, L.bo, 1.f, L.ln2_g, L.ln2_b, nullptr, nullptr, 1, w.h);   // pre-LN
+    // pre-LN
+    if (fuse_wo) c.ln(512, 8, L.bo, 1.f, L.ln2_g, L.ln2_b, nullptr, nullptr, 1, w.h);
+    else c.branch_ln(w.ctx, 512, L.wo, 512, L.bo, 1.f, L.ln2_g, L.ln2_b, nullptr, nullptr, 1, w.h);
     c.lin(w.h, 512, L.w1, L.b1, 2048, 512, w.big, 2048, EPI_GELU, bf);
-    ns = c.branch(w.big, 2048, L.w2, 512, 2048);
     if (l < 30)
-      c.ln(512, ns, L.b2, 1.f, m->rl[l + 1].ln1_g, m->rl[l + 1].ln1_b, nullptr, nullptr, 1, w.h);
-    else
-      c.ln(512, ns, L.b2, 1.f, m->fin_g, m->fin_b, nullptr, nullptr, 2, nullptr);  // final LN
+      c.branch_ln(w.big, 2048, L.w2, 2048, L.b2, 1.f, m->rl[l + 1].ln1_g, m->rl[l + 1].ln1_b,
+                  nullptr, nullptr, 1, w.h);
+    else  // final LN, into x
+      c.branch_ln(w.big, 2048, L.w2, 2048, L.b2, 1.f, m->fin_g, m->fin_b, nullptr, nullptr, 2,
+                  nullptr);
     tp.at(l, SF_TAP_LAYER_OUT, w.x, false, 512);
   }
   head_nemotron(w.x, B * W, m->nh_w, m->nh_b, m->up_w, m->up_b, w.probs, w.probs10, s);
