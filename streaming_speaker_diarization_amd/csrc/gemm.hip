@@ -882,11 +882,13 @@ int gemm_glu_dwconv(const GemmArgs& g, hipStream_t s) {
 }
 
 int gemm_resid(const GemmArgs& g, hipStream_t s) {
-  if (g.M <= SLICE_MAX_ROWS || g.K % SF_BIG_BK || g.N % 128 || g.K <= 0) return -1;
+  if (g.M <= SLICE_MAX_ROWS || g.K % SF_BIG_BK || g.N % 64 || g.K <= 0) return -1;
+  // 128 x 64 tiles: the N = 512 branches then make about three rounds of
+  // workgroups over the CUs rather than one and a half
   klaunch(PROF_GEMM, 2.0 * g.M * g.N * g.K,
           2.0 * ((double)g.M * g.K + (double)g.N * g.K) + 8.0 * g.M * g.N,
-          gemm_big_kernel<float, EPI_RESID, 128, SF_BIG_BK, SF_BIG_NST>,
-          dim3(g.N / 128, (g.M + 127) / 128), dim3(256), s, g);
+          gemm_big_kernel<float, EPI_RESID, 64, SF_BIG_BK, SF_BIG_NST>,
+          dim3(g.N / 64, (g.M + 127) / 128), dim3(256), s, g);
   return 1;
 }
 

@@ -43,7 +43,7 @@ struct GemmArgs {
 // returns the slice count; other epilogues return 1.
 int gemm(const GemmArgs& g, int epi, bool bf16_in, bool bf16_out, hipStream_t s);
 // Residual branch of batched windows (bf16 A and W, more than 4096 rows,
-// K % 64 == 0, N % 128 == 0): out (fp32, ldo) += ralpha * (A W^T + bias), in
+// K % 64 == 0, N % 64 == 0): out (fp32, ldo) += ralpha * (A W^T + bias), in
 // place, with the arithmetic of a LayerNorm that folds in one partial slice.
 // Returns 1, or -1 (nothing launched) for other shapes.
 int gemm_resid(const GemmArgs& g, hipStream_t s);
