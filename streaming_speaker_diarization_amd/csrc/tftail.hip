@@ -179,16 +179,18 @@ __global__ __launch_bounds__(NW * 64) void tf_tail_kernel(TfTailArgs a) {
 // ---------------------------------------------------------------------------
 // Throughput form (batched windows, more than 4096 rows): the whole layer tail
 //   x1 = LN1(x + ctx Wo^T + bo),  x <- LN2(x1 + relu(x1 W1^T + b1) W2^T + b2)
-// in one kernel, h <- x as the next GEMM operand (bf16). One workgroup = 64
-// rows; wave w owns output columns 48w .. 48w+47 of every 192-wide product
-// (3 tiles x 4 row tiles, so each weight fragment it loads feeds 4 products)
-// and, in each of the 4 hidden chunks of 192, hidden columns 48w .. 48w+47.
+// in one kernel, h <- x as the next GEMM operand (bf16). One workgroup = 48
+// rows (each wave's chain of products is the kernel's limit, so the rows go
+// to as many workgroups as two per CU allow); wave w owns output columns
+// 48w .. 48w+47 of every 192-wide product (3 tiles x 3 row tiles, so each
+// weight fragment it loads feeds 3 products) and, in each of the 4 hidden
+// chunks of 192, hidden columns 48w .. 48w+47.
 // The A operands (ctx, then x1, and each hidden chunk) sit in LDS as bf16 for
 // all four waves; row statistics of both LayerNorms are reduced across the
 // waves through LDS. The output projection of the hidden layer accumulates
 // over the chunks in registers, so no partial sums leave the kernel.
 namespace {
-constexpr int TB_RB = 64, TB_NW = 4, TB_CT = 3, TB_RT = TB_RB / 16, TB_NK = TD / 32;
+constexpr int TB_RB = 48, TB_NW = 4, TB_CT = 3, TB_RT = TB_RB / 16, TB_NK = TD / 32;
 }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -208,8 +210,9 @@ void tf_layer_tp_kernel(TfLayerArgs a) {
     const bf16_t* ctx = static_cast<const bf16_t*>(a.ctx);
     constexpr int CPR = TD / 8;  // 24 chunks per row
 #pragma unroll
-    for (int i = 0; i < TB_RB * CPR / 256; ++i) {
+    for (int i = 0; i < (TB_RB * CPR + 255) / 256; ++i) {
       const int c = tid + 256 * i, r = c / CPR, q = c % CPR;
+      if (c >= TB_RB * CPR) break;
       const int row = min(r0 + r, a.M - 1);
       *reinterpret_cast<vec16*>(&As[r * TLH + 8 * q]) =
           *reinterpret_cast<const vec16*>(ctx + (size_t)row * TD + 8 * q);
@@ -432,9 +435,9 @@ void tf_layer_tp_kernel(TfLayerArgs a) {
     if (pass < 2) {
       constexpr int CPR = TD / 8;
 #pragma unroll
-      for (int i = 0; i < TB_RB * CPR / 256; ++i) {
+      for (int i = 0; i < (TB_RB * CPR + 255) / 256; ++i) {
         const int c = tq + 256 * i, r = c / CPR, q = c % CPR, row = r0 + r;
-        if (row < a.M)
+        if (c < TB_RB * CPR && row < a.M)
           *reinterpret_cast<vec16*>(qkv + (size_t)row * (3 * TD) + TD * pass + 8 * q) =
               *reinterpret_cast<const vec16*>(&Hs[r * TLH + 8 * q]);
       }
@@ -474,8 +477,8 @@ void tf_layer_tp_kernel(TfLayerArgs a) {
     } else {
       // windows shorter than the block: 8-row runs of one V column
 #pragma unroll 1
-      for (int i = 0; i < TD * (TB_RB / 8) / 256; ++i) {
-        const int c = tq + 256 * i, col = c >> 3, r = (c & 7) * 8, row = r0 + r;
+      for (int c = tq; c < TD * (TB_RB / 8); c += 256) {
+        const int col = c / (TB_RB / 8), r = c % (TB_RB / 8) * 8, row = r0 + r;
         if (row >= a.M) continue;
         const int hh = col / 24, d = col % 24;
         for (int e = 0; e < 8 && row + e < a.M; ++e) {
