@@ -494,24 +494,28 @@ void attn_tp_kernel(AttnArgs a) {
 
   // ---- one tile's K, V^T and band chunks into registers (clamped, unconditional)
   vec16 rk[NCK], rv[NCV], rbd[NCB > 0 ? NCB : 1];
+  // element offsets in 32 bits (the batch holds at most 64 x 1024 rows of
+  // at most 1536 columns, the position table 2047 x 512)
+  const bf16_t* kbase = qkv + rowbase * a.ldq + a.koff + h * HD;
+  const bf16_t* pbase = P + h * HD;
   auto fetch = [&](int j0) {
 #pragma unroll
     for (int i = 0; i < NCK; ++i) {
       const int c = tid + 256 * i, r = c / CPK, q = c % CPK;
       const int j = min(j0 + r, a.W - 1), d = min(8 * q, HD - 8);
-      rk[i] = *reinterpret_cast<const vec16*>(qkv + (rowbase + j) * a.ldq + a.koff + h * HD + d);
+      rk[i] = *reinterpret_cast<const vec16*>(kbase + (j * a.ldq + d));
     }
 #pragma unroll
     for (int i = 0; i < NCV; ++i) {
       const int c = tid + 256 * i, d = c / 8, q = c % 8;
-      rv[i] = *reinterpret_cast<const vec16*>(vtb + (size_t)min(d, HD - 1) * a.vpitch +
-                                               min(j0 + 8 * q, a.vpitch - 8));
+      rv[i] = *reinterpret_cast<const vec16*>(vtb + (min(d, HD - 1) * a.vpitch +
+                                                     min(j0 + 8 * q, a.vpitch - 8)));
     }
 #pragma unroll
     for (int i = 0; i < NCB; ++i) {
       const int c = tid + 256 * i, r = c / CPK, q = c % CPK;
       const int pr = min(max(iq0 - j0 - 63 + r + a.p_center, 0), 2 * a.p_center);
-      rbd[i] = *reinterpret_cast<const vec16*>(P + (size_t)pr * a.ldp + h * HD + 8 * q);
+      rbd[i] = *reinterpret_cast<const vec16*>(pbase + (pr * a.ldp + 8 * q));
     }
   };
   // zero what lies outside the head, the window or the position table; V^T
@@ -581,20 +585,10 @@ void attn_tp_kernel(AttnArgs a) {
     // staging arrays in registers), in flight while this tile is used
     fetch(min(j0 + 64, (ntile - 1) * 64));
 
-    // ---- S^T: lane (g, c16) holds keys j0 + 16nt + 4g + r of its query
+    // ---- S^T: lane (g, c16) holds keys j0 + 16nt + 4g + r of its query. With
+    // relative positions the accumulators start from the position term, so
+    // the K Q^T products add onto it.
     f32x4 S[2][4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      S[0][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      S[1][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < NQF; ++ks) {
-        const bf16x8_t kf =
-            *reinterpret_cast<const bf16x8_t*>(&Ks[(16 * nt + c16) * LK + ks * 32 + 8 * g]);
-        S[0][nt] = M_::mma(kf, qa[0][ks], S[0][nt]);
-        S[1][nt] = M_::mma(kf, qa[1][ks], S[1][nt]);
-      }
-    }
     if constexpr (REL) {
       // G^T[rho][c] = p(delta).(q_c + v) with band row 32w + 16s + rho <->
       // delta = (iw + 16s) - j0 - 63 + rho; the score of (query c, key k)
@@ -622,10 +616,25 @@ void attn_tp_kernel(AttnArgs a) {
         for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            S[s][nt][r] += G[(c16 - 16 * nt - 4 * g - r + 63) * GP + c16];
+            S[s][nt][r] = G[(c16 - 16 * nt - 4 * g - r + 63) * GP + c16];
         wave_lds_sync();  // the next set rewrites G
       }
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        S[0][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        S[1][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < NQF; ++ks) {
+        const bf16x8_t kf =
+            *reinterpret_cast<const bf16x8_t*>(&Ks[(16 * nt + c16) * LK + ks * 32 + 8 * g]);
+        S[0][nt] = M_::mma(kf, qa[0][ks], S[0][nt]);
+        S[1][nt] = M_::mma(kf, qa[1][ks], S[1][nt]);
+      }
 
     // ---- online softmax (log2 domain: the running max is kept scaled by
     // scale*log2(e), p = 2^(s*scale*log2(e) - m)); P^T as the B operand of
