@@ -299,7 +299,7 @@ def pmc_summary(name, fetch_dir, write_dir, copy_dir):
         # the fp32 relative-position table GEMM and its split-K reduction run
         # once while the model initialises, before the probed windows
         init = n.startswith("gemm_slice_kernel<float") or n.startswith("splitk_epi")
-        return n.startswith(("gemm_", "splitk_epi", "tf_tail")) and not init
+        return n.startswith(("gemm_", "splitk_epi", "tf_tail", "tf_layer_tp")) and not init
 
     n = sum(v[0] for k, v in fe.items() if is_gemm(k))
     rd = sum(v[1] for k, v in fe.items() if is_gemm(k)) * 1024 * f_scale / max(n, 1)
@@ -317,7 +317,7 @@ def pmc_summary(name, fetch_dir, write_dir, copy_dir):
              "  timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE -f csv -d COPY/copy_fetch -o run -- python3 R/bench.py --copy-probe 1024",
              "  timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE -f csv -d COPY/copy_write -o run -- python3 R/bench.py --copy-probe 1024",
              f"  python3 R/bench.py{wk} --pmc-summary FETCH WRITE COPY", "",
-             "GEMM class: every gemm_*, splitk_epi and tf_tail dispatch of the probed windows (the",
+             "GEMM class: every gemm_*, splitk_epi, tf_tail and tf_layer_tp dispatch of the probed windows (the",
              "relative-position table GEMM and its reduction, run once at model initialisation, excluded).", "",
              f"Calibration (1 GiB device copy {ck[0]}): FETCH_SIZE scale {f_scale:.4f}, "
              f"WRITE_SIZE scale {w_scale:.4f}", "",
