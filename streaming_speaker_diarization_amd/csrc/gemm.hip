@@ -902,7 +902,9 @@ int gemm(const GemmArgs& g, int epi, bool bf16_in, bool bf16_out, hipStream_t s)
     return checked(bf16_in ? launch<bf16_t, float, EPI_PARTIAL>(g, s)
                            : launch<float, float, EPI_PARTIAL>(g, s));
   if (epi == EPI_GLU)
-    return checked(bf16_in ? launch<bf16_t, float, EPI_GLU>(g, s) : launch<float, float, EPI_GLU>(g, s));
+    return checked(!bf16_in    ? launch<float, float, EPI_GLU>(g, s)
+                   : bf16_out ? launch<bf16_t, bf16_t, EPI_GLU>(g, s)
+                              : launch<bf16_t, float, EPI_GLU>(g, s));
   if (bf16_in)
     return checked(bf16_out ? launch_epi<bf16_t, bf16_t>(g, epi, s) : launch_epi<bf16_t, float>(g, epi, s));
   return checked(bf16_out ? launch_epi<float, bf16_t>(g, epi, s) : launch_epi<float, float>(g, epi, s));

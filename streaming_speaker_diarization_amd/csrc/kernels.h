@@ -129,9 +129,11 @@ struct TfLayerArgs {
 };
 void tf_layer_tp(const TfLayerArgs& a, hipStream_t s);
 
-// nv (may be null): device copy of n_valid, read instead when given
-void dwconv_time(const float* glu, int B, int W, int n_valid, const int* nv, const float* w9,
-                 const float* scale, const float* shift, void* out, bool bf16, hipStream_t s);
+// nv (may be null): device copy of n_valid, read instead when given. glu is
+// (B*W, 512), fp32 or (glu_bf16, with a bf16 output only) bf16.
+void dwconv_time(const void* glu, bool glu_bf16, int B, int W, int n_valid, const int* nv,
+                 const float* w9, const float* scale, const float* shift, void* out, bool bf16,
+                 hipStream_t s);
 
 void logmel(const float* audio, long long a_bstride, long long ring_mask, long long n_total,
             long long t0, int nfr, int B, const float* tables, float* mel, long long m_bstride,

@@ -148,11 +148,12 @@ void layernorm(const LnArgs& a, bool bf16, hipStream_t s) {
 // beyond n_valid (and outside the window) count as zero. BatchNorm and the
 // conv bias are folded into scale/shift. One workgroup = R frames of one
 // stream; a thread owns 4 channels and keeps the R + 8 input rows of them in
-// registers (16-byte loads, each input row loaded once). R = 4 for one or a
-// few windows (enough workgroups to fill the chip), 16 for batched windows
-// (1.5 rows read per row written instead of 3).
-template <typename T, int R>
-__global__ __launch_bounds__(128) void dwconv_time_kernel(const float* glu, int W, int n_valid_h,
+// registers (each input row loaded once). R = 4 for one or a few windows
+// (enough workgroups to fill the chip), 16 for batched windows (1.5 rows read
+// per row written instead of 3). The GLU output arrives as TI (fp32, or bf16
+// in batched bf16 windows).
+template <typename TI, typename T, int R>
+__global__ __launch_bounds__(128) void dwconv_time_kernel(const TI* glu, int W, int n_valid_h,
                                                           const int* nv, const float* w9,
                                                           const float* sc, const float* sh, T* out) {
   const int n_valid = nv ? *nv : n_valid_h;
@@ -169,11 +170,19 @@ __global__ __launch_bounds__(128) void dwconv_time_kernel(const float* glu, int 
     b = t / gx;
   }
   const int c = threadIdx.x * 4;
-  const float* gb = glu + (size_t)b * W * 512 + c;
+  const TI* gb = glu + (size_t)b * W * 512 + c;
   float4 x[R + 8];
 #pragma unroll
-  for (int j = 0; j < R + 8; ++j)
-    x[j] = *reinterpret_cast<const float4*>(gb + (size_t)min(max(t0 + j - 4, 0), W - 1) * 512);
+  for (int j = 0; j < R + 8; ++j) {
+    const TI* src = gb + (size_t)min(max(t0 + j - 4, 0), W - 1) * 512;
+    if constexpr (sizeof(TI) == 4) {
+      x[j] = *reinterpret_cast<const float4*>(src);
+    } else {
+      const uint2 u = *reinterpret_cast<const uint2*>(src);
+      x[j] = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                         __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+    }
+  }
   float4 wk[9];  // w[c..c+3][k] for tap k, from the [c][9] layout
   {
     float wr[36];
@@ -216,19 +225,27 @@ __global__ __launch_bounds__(128) void dwconv_time_kernel(const float* glu, int 
   }
 }
 
-void dwconv_time(const float* glu, int B, int W, int n_valid, const int* nv, const float* w9,
-                 const float* sc, const float* sh, void* out, bool bf16, hipStream_t s) {
+void dwconv_time(const void* glu, bool glu_bf16, int B, int W, int n_valid, const int* nv,
+                 const float* w9, const float* sc, const float* sh, void* out, bool bf16,
+                 hipStream_t s) {
   if (W <= 0) return;
-  const double fl = 2.0 * 9 * 512 * B * W, by = (double)B * W * 512 * (4.0 + (bf16 ? 2 : 4));
+  const double fl = 2.0 * 9 * 512 * B * W,
+               by = (double)B * W * 512 * ((glu_bf16 ? 2.0 : 4.0) + (bf16 ? 2 : 4));
   auto go = [&](auto rows) {
     constexpr int R = decltype(rows)::value;
     dim3 grid((W + R - 1) / R, B);
-    if (bf16)
-      klaunch(PROF_CONV, fl, by, dwconv_time_kernel<bf16_t, R>, grid, dim3(128), s, glu, W, n_valid,
-              nv, w9, sc, sh, static_cast<bf16_t*>(out));
+    if (glu_bf16 && bf16)
+      klaunch(PROF_CONV, fl, by, dwconv_time_kernel<bf16_t, bf16_t, R>, grid, dim3(128), s,
+              static_cast<const bf16_t*>(glu), W, n_valid, nv, w9, sc, sh,
+              static_cast<bf16_t*>(out));
+    else if (bf16)
+      klaunch(PROF_CONV, fl, by, dwconv_time_kernel<float, bf16_t, R>, grid, dim3(128), s,
+              static_cast<const float*>(glu), W, n_valid, nv, w9, sc, sh,
+              static_cast<bf16_t*>(out));
     else
-      klaunch(PROF_CONV, fl, by, dwconv_time_kernel<float, R>, grid, dim3(128), s, glu, W, n_valid,
-              nv, w9, sc, sh, static_cast<float*>(out));
+      klaunch(PROF_CONV, fl, by, dwconv_time_kernel<float, float, R>, grid, dim3(128), s,
+              static_cast<const float*>(glu), W, n_valid, nv, w9, sc, sh,
+              static_cast<float*>(out));
   };
   if ((size_t)B * W > 4096) go(std::integral_constant<int, 16>{});
   else go(std::integral_constant<int, 4>{});

@@ -682,8 +682,9 @@ static void encode_sortformer(const sf_model* m, EncWs& w, int B, int W, int n_v
       gemm_glu_dwconv(g, s);
       c.branch_ln(w.ctx, 512, L.pw2, 512, L.pw2_b, 1.f, L.ff2_g, L.ff2_b, nullptr, nullptr, 1, w.h);
     } else {
-      c.lin(w.h, 512, L.pw1, L.pw1_b, 1024, 512, w.glu, 512, EPI_GLU, false);
-      dwconv_time(w.glu, B, W, n_valid, nv, L.dw9, L.dw_sc, L.dw_sh, w.h, bf, s);
+      // (batched bf16 windows: the GLU output goes to the depthwise conv as bf16)
+      c.lin(w.h, 512, L.pw1, L.pw1_b, 1024, 512, w.glu, 512, EPI_GLU, bf);
+      dwconv_time(w.glu, bf, B, W, n_valid, nv, L.dw9, L.dw_sc, L.dw_sh, w.h, bf, s);
       c.branch_ln(w.h, 512, L.pw2, 512, L.pw2_b, 1.f, L.ff2_g, L.ff2_b, nullptr, nullptr, 1, w.h);
     }
     // macaron FFN, second half, then the output LayerNorm (fused with the
