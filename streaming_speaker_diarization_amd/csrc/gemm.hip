@@ -458,23 +458,33 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs g) {
   const int t = xcd * q8 + min(xcd, r8) + pid / 8;
   const int n0 = (t % gx) * BN, m0 = (t / gx) * BM;
 
-  const bf16_t* A = static_cast<const bf16_t*>(g.A);
-  const bf16_t* Wt = static_cast<const bf16_t*>(g.W);
-  // this lane's row within a DMA block and the global chunk it fetches
+  const char* A = static_cast<const char*>(g.A);
+  const char* Wt = static_cast<const char*>(g.W);
+  // this lane's row within a DMA block and the global chunk it fetches; its
+  // byte offset within the operand (32 bits: the launcher keeps both operands
+  // under 4 GiB) is fixed, and each K tile moves a workgroup-uniform base, so
+  // the loads take a scalar base and the wave's LDS blocks scalar addresses
   const int lr = lane / CPR, lc = (lane % CPR) ^ (lr % CPR);
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t goff[LOADS];
+#pragma unroll
+  for (int j = 0; j < LOADS; ++j) {
+    const int blk = wv * LOADS + j;  // A blocks first, then B blocks
+    if (blk < A_BLK) {
+      const int r = min(m0 + blk * RPB + lr, g.M - 1);
+      goff[j] = ((uint32_t)r * (uint32_t)g.lda + lc * 8) * 2u;
+    } else {
+      const int r = n0 + (blk - A_BLK) * RPB + lr;
+      goff[j] = ((uint32_t)r * (uint32_t)g.ldw + lc * 8) * 2u;
+    }
+  }
   auto issue = [&](int kt) {
     char* st = smem + (kt % NST) * STAGE;
-    const int k0 = kt * BK + lc * 8;
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
-      const int blk = wave * LOADS + j;  // A blocks first, then B blocks
-      if (blk < A_BLK) {
-        const int r = min(m0 + blk * RPB + lr, g.M - 1);
-        lds_dma16(A + (size_t)r * g.lda + k0, st + blk * 1024);
-      } else {
-        const int r = n0 + (blk - A_BLK) * RPB + lr;
-        lds_dma16(Wt + (size_t)r * g.ldw + k0, st + blk * 1024);
-      }
+      const int blk = wv * LOADS + j;
+      const char* base = (blk < A_BLK ? A : Wt) + (size_t)kt * (BK * 2);
+      lds_dma16(base + goff[j], st + blk * 1024);
     }
   };
 
@@ -778,6 +788,11 @@ static void slice_launch(const GemmArgs& g, int ns, hipStream_t s) {
   }
 }
 
+// gemm_big_kernel addresses its operands with 32-bit byte offsets
+static bool big_offsets_fit(const GemmArgs& g) {
+  return (uint64_t)g.M * g.lda * 2 < (1ull << 32) && (uint64_t)g.N * g.ldw * 2 < (1ull << 32);
+}
+
 template <typename T, typename OutT, int EPI>
 static void launch_kernel(const GemmArgs& g, int ns, hipStream_t s) {
   const int ks = g.K / ns;
@@ -793,7 +808,8 @@ static void launch_kernel(const GemmArgs& g, int ns, hipStream_t s) {
           else slice_launch<T, OutT, EPI, 512>(g, ns, s);
         }
     }
-  } else if (sizeof(T) == 2 && ns == 1 && g.K % SF_BIG_BK == 0 && g.N % 64 == 0) {
+  } else if (sizeof(T) == 2 && ns == 1 && g.K % SF_BIG_BK == 0 && g.N % 64 == 0 &&
+             big_offsets_fit(g)) {
     if constexpr (sizeof(T) == 2) {
       if (g.N % 128 == 0)
         klaunch(PROF_GEMM, g_flops, g_bytes, gemm_big_kernel<OutT, EPI, 128, SF_BIG_BK, SF_BIG_NST>,
@@ -882,7 +898,8 @@ int gemm_glu_dwconv(const GemmArgs& g, hipStream_t s) {
 }
 
 int gemm_resid(const GemmArgs& g, hipStream_t s) {
-  if (g.M <= SLICE_MAX_ROWS || g.K % SF_BIG_BK || g.N % 64 || g.K <= 0) return -1;
+  if (g.M <= SLICE_MAX_ROWS || g.K % SF_BIG_BK || g.N % 64 || g.K <= 0 || !big_offsets_fit(g))
+    return -1;
   // 128 x 64 tiles: the N = 512 branches then make about three rounds of
   // workgroups over the CUs rather than one and a half
   klaunch(PROF_GEMM, 2.0 * g.M * g.N * g.K,
