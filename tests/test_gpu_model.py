@@ -145,6 +145,25 @@ def test_encode_window_bf16_batched_throughput_regime(sfbf, wbf):
         assert err <= 2e-2 and agree >= 0.995
 
 
+@pytest.mark.parametrize("B,W,nv", [(160, 30, 27), (45, 100, 93)])
+def test_encode_window_bf16_batched_short_windows(sfbf, wbf, B, W, nv):
+    """Batches of short windows above 4096 rows: the batched kernels' paths for
+    windows shorter than their row tiles (V^T stores of the Q/K/V GEMM below
+    128 rows per window, of the transformer tail below 48) against the oracle
+    on sampled streams; rows past n_valid hold garbage."""
+    full = OR.pre_encode_all(make_weights("sortformer", 0, bf16=True),
+                             OF.log_mel(workload_audio("low60s")))
+    span = full.shape[0] - W
+    xs = np.stack([full[(17 * b) % span:(17 * b) % span + W] for b in range(B)])
+    xs[:, nv:] = np.random.default_rng(B).standard_normal((B, W - nv, 512))
+    got = sfbf.encode_window(_cuda(xs), n_valid=nv).cpu().numpy()
+    for b in (0, B // 2 + 1, B - 1):
+        ref = OS.encode_window(wbf, xs[b], n_valid=nv)
+        err, agree = _report(f"window bf16 batched B={B} W={W} valid={nv} b={b}", got[b, :nv],
+                             ref[:nv])
+        assert err <= 2e-2 and agree >= 0.995
+
+
 def test_nemotron_window_fp32_and_bf16(rt, emb20):
     m = rt.Model("nemotron", "f32", seed=1)
     w = make_weights("nemotron", 1)
