@@ -716,7 +716,7 @@ static void encode_sortformer(const sf_model* m, EncWs& w, int B, int W, int n_v
     a.ctx = w.ctx; a.ldc = 192; a.scale = 1.0f / std::sqrt(24.0f);
     attention(a, ATT_PLAIN, 24, bf, s);
     tp.at(17 + l, SF_TAP_ATTN_CTX, w.ctx, bf, 192);
-    if (bf && B * W <= SLICE_MAX_ROWS) {
+    if (bf && !tail_qkv) {
       // output projection, LN1 and the FFN's two Linears in one kernel (x1 kept
       // in the fp32 GLU buffer, which the transformer does not otherwise use)
       TfTailArgs t{};
@@ -729,7 +729,7 @@ static void encode_sortformer(const sf_model* m, EncWs& w, int B, int W, int n_v
       n.part = w.part; n.nsplit = nc; n.pbias = L.b2; n.alpha = 1.f;
       n.g1 = L.ln2_g; n.b1 = L.ln2_b; n.x_mode = 2; n.y_act = w.h;
       layernorm(n, bf, s);
-    } else if (bf) {
+    } else if (tail_qkv) {
       // batched windows: the whole tail in one kernel
       TfLayerArgs t{};
       t.ctx = w.ctx; t.x = w.x; t.xo = w.x; t.h = w.h; t.M = B * W;
