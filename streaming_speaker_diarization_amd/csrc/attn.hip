@@ -431,6 +431,9 @@ void attn_tp_kernel(AttnArgs a) {
   constexpr int LV = 64 + 8;               // V^T row pitch
   constexpr int GP = 20;                   // G^T row pitch (fp32), conflict-free both ways
   constexpr bool REL = MODE == ATT_RELPOS;
+  // a padded head keeps a row of ones in V^T at dim HD: the O^T product then
+  // accumulates each query's softmax denominator with its own rescaling
+  constexpr bool ONES = HD < HDP;
   constexpr int QB = 128;                  // query rows per workgroup
   constexpr int NB = REL ? QB + 64 : 0;    // band rows per key tile
   constexpr int CPK = HDP / 8;             // 16-byte chunks per K / band row
@@ -537,7 +540,7 @@ void attn_tp_kernel(AttnArgs a) {
       const int c = tid + 256 * i, d = c / 8, q = c % 8, j = j0 + 8 * q;
       uint32_t m[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) m[e] = d < HD ? rv[i].w[e] : 0u;
+      for (int e = 0; e < 4; ++e) m[e] = d < HD ? rv[i].w[e] : ONES && d == HD ? 0x3F803F80u : 0u;
       if (vedge) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -665,17 +668,17 @@ void attn_tp_kernel(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           p[nt][r] = __builtin_amdgcn_exp2f(fmaf(S[s][nt][r], sl2, -mnew));
-          rs += p[nt][r];
+          if constexpr (!ONES) rs += p[nt][r];
         }
       if (__ballot(mnew != mrow[s])) {  // rescale only when some query's max moved
         const float alpha = __builtin_amdgcn_exp2f(mrow[s] - mnew);
-        lrow[s] *= alpha;
+        if constexpr (!ONES) lrow[s] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
           for (int r = 0; r < 4; ++r) O[s][dt][r] *= alpha;
       }
-      lrow[s] += rs;
+      if constexpr (!ONES) lrow[s] += rs;
       mrow[s] = mnew;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -703,9 +706,14 @@ void attn_tp_kernel(AttnArgs a) {
   bf16_t* ctx = static_cast<bf16_t*>(a.ctx);
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    float l = lrow[s];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    float l;
+    if constexpr (ONES) {  // dim HD of query c16 sits in lane group (HD % 16) / 4
+      l = __shfl(O[s][HD / 16][HD % 4], 16 * ((HD % 16) / 4) + c16);
+    } else {
+      l = lrow[s];
+      l += __shfl_xor(l, 16);
+      l += __shfl_xor(l, 32);
+    }
     const int i = iw + 16 * s + c16;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
