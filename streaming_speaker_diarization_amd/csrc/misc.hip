@@ -196,20 +196,33 @@ __global__ __launch_bounds__(128) void dwconv_time_kernel(const TI* glu, int W, 
   }
   const float4 s4 = *reinterpret_cast<const float4*>(sc + c);
   const float4 h4 = *reinterpret_cast<const float4*>(sh + c);
+  // every tap of every row of the block inside [0, n_valid): no masking
+  const bool interior = t0 >= 4 && t0 + R + 4 <= n_valid;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int t = t0 + r;
     if (t >= W) break;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (interior) {
 #pragma unroll
-    for (int k = 0; k < 9; ++k) {
-      const int tt = t + k - 4;
-      const bool live = tt >= 0 && tt < n_valid;
-      const float4 v = x[r + k];
-      acc.x += live ? wk[k].x * v.x : 0.f;
-      acc.y += live ? wk[k].y * v.y : 0.f;
-      acc.z += live ? wk[k].z * v.z : 0.f;
-      acc.w += live ? wk[k].w * v.w : 0.f;
+      for (int k = 0; k < 9; ++k) {
+        const float4 v = x[r + k];
+        acc.x = fmaf(wk[k].x, v.x, acc.x);
+        acc.y = fmaf(wk[k].y, v.y, acc.y);
+        acc.z = fmaf(wk[k].z, v.z, acc.z);
+        acc.w = fmaf(wk[k].w, v.w, acc.w);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 9; ++k) {
+        const int tt = t + k - 4;
+        const bool live = tt >= 0 && tt < n_valid;
+        const float4 v = x[r + k];
+        acc.x += live ? wk[k].x * v.x : 0.f;
+        acc.y += live ? wk[k].y * v.y : 0.f;
+        acc.z += live ? wk[k].z * v.z : 0.f;
+        acc.w += live ? wk[k].w * v.w : 0.f;
+      }
     }
     float y[4] = {swishf_(s4.x * acc.x + h4.x), swishf_(s4.y * acc.y + h4.y),
                   swishf_(s4.z * acc.z + h4.z), swishf_(s4.w * acc.w + h4.w)};
